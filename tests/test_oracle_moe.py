@@ -1,0 +1,267 @@
+"""Pins for the MoE-level oracle (CPU only): validator, router, permutation,
+fp64 GEMM reference, SiLU*mul, combine, calibration, workload generators.
+
+Pinned by enumerated special values, brute force with Python ``sorted`` and
+triple loops, closed forms (all-ones / one-hot operands, silu values), and
+structural properties of the synthetic workloads.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import formats as F
+from oracle import moe as M
+from oracle import quant as Q
+import synthetic as S
+
+
+# --- validator ---------------------------------------------------------------
+
+def _f32_from_bits(b):
+    return np.array([b], dtype=np.uint32).view(np.float32)[0]
+
+
+def test_validator_reasons():
+    vals = np.array([0.5, np.nan, np.inf, -np.inf, 0.0, -0.0, -1.0,
+                     _f32_from_bits(0x00000001),      # smallest subnormal: 1/x overflows
+                     _f32_from_bits(0x00200000),      # ~2.9e-39: 1/x overflows
+                     _f32_from_bits(0x00400000),      # ~5.9e-39: 1/x finite
+                     1.0e-3, 3.0], dtype=np.float32)
+    written = np.ones(vals.size, dtype=np.uint8)
+    written[-1] = 0                                   # valid-looking stale value
+    ok, gs, st = M.validate_scales(vals, written)
+    assert not ok and gs is None
+    assert st.tolist() == [M.SLOT_OK, M.SLOT_NAN, M.SLOT_INF, M.SLOT_INF, M.SLOT_NONPOSITIVE,
+                           M.SLOT_NONPOSITIVE, M.SLOT_NONPOSITIVE, M.SLOT_RECIP_OVERFLOW,
+                           M.SLOT_RECIP_OVERFLOW, M.SLOT_OK, M.SLOT_OK, M.SLOT_UNWRITTEN]
+
+
+def test_validator_success_gives_reciprocals():
+    vals = np.array([0.5, 3.0, 1.0 / 2688, 7.0e-39], dtype=np.float32)
+    ok, gs, st = M.validate_scales(vals)
+    assert ok and np.all(st == 0)
+    for v, g in zip(vals, gs):
+        assert g == np.float32(np.float32(1) / v)
+    assert gs[0] == 2.0
+
+
+# --- router / permutation -----------------------------------------------------
+
+def test_route_brute_force_with_ties():
+    rng = np.random.default_rng(3)
+    logits = rng.integers(-3, 4, size=(50, 9)).astype(np.float32)    # many ties
+    logits[0] = 0.0
+    logits[1, 4] = -0.0
+    ids, w = M.route(logits, 3)
+    for t in range(50):
+        order = sorted(range(9), key=lambda e: (-float(logits[t, e]), e))
+        assert ids[t].tolist() == order[:3]
+        sel = [float(logits[t, e]) for e in order[:3]]
+        ex = [math.exp(s - max(sel)) for s in sel]
+        assert np.allclose(w[t], [x / sum(ex) for x in ex], rtol=1e-15, atol=0)
+    assert ids[0].tolist() == [0, 1, 2]
+
+
+def test_permute_brute_force():
+    rng = np.random.default_rng(4)
+    T, k, E = 40, 3, 7
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    ids[:, :][ids == 5] = 6          # expert 5 empty
+    for t in range(T):               # keep per-token ids distinct after the remap
+        if len(set(ids[t].tolist())) < k:
+            ids[t] = [0, 1, 2]
+    offsets, src, inv = M.permute(ids, E)
+    pairs = sorted(range(T * k), key=lambda q: (int(ids.reshape(-1)[q]), q))
+    assert src.tolist() == pairs
+    for e in range(E):
+        assert offsets[e] == sum(1 for q in range(T * k) if ids.reshape(-1)[q] < e)
+    assert offsets[5] == offsets[6]
+    assert np.array_equal(inv[src], np.arange(T * k))
+
+
+# --- GEMM reference ------------------------------------------------------------
+
+def _rand_nvfp4(rng, R, K):
+    codes = rng.integers(0, 256, size=(R, K // 2)).astype(np.uint8)
+    sf = rng.integers(0, 0x7F, size=(R, K // 16)).astype(np.uint8)
+    return codes, sf
+
+
+def test_grouped_gemm_brute_force():
+    rng = np.random.default_rng(5)
+    E, N, K = 3, 5, 32
+    offsets = np.array([0, 2, 2, 6], dtype=np.int32)          # expert 1 has no rows
+    ac, asf = _rand_nvfp4(rng, 6, K)
+    wc = np.stack([_rand_nvfp4(rng, N, K)[0] for _ in range(E)])
+    ws = np.stack([_rand_nvfp4(rng, N, K)[1] for _ in range(E)])
+    alpha = np.array([0.5, 2.0, 3.0])
+    got = M.grouped_gemm_ref(ac, asf, offsets, wc, ws, alpha)
+
+    def val(codes, sf, r, kk):
+        byte = int(codes[r, kk // 2])
+        c = byte & 0xF if kk % 2 == 0 else byte >> 4
+        return F.e2m1_decode(c) * F.e4m3_decode(int(sf[r, kk // 16]))
+
+    for p in range(6):
+        e = 0 if p < 2 else 2
+        for n in range(N):
+            acc = 0.0
+            for kk in range(K):
+                acc += val(ac, asf, p, kk) * val(wc[e], ws[e], n, kk)
+            assert got[p, n] == pytest.approx(alpha[e] * acc, rel=1e-14, abs=1e-12)
+    sub = M.grouped_gemm_ref(ac, asf, offsets, wc, ws, alpha, rows=[5, 0])
+    assert np.array_equal(sub, got[[5, 0]])
+
+
+def test_gemm_all_ones_and_one_hot():
+    K, N = 64, 4
+    ones = np.full((1, K // 2), 0x22, dtype=np.uint8)           # every code = 1.0
+    unit = np.full((1, K // 16), 0x38, dtype=np.uint8)          # scale 1.0
+    w = np.zeros((1, N, K // 2), dtype=np.uint8)
+    w[0, 2, 3] = 0x70                                            # element k=7 of row 2 = 6.0
+    ws = np.full((1, N, K // 16), 0x38, dtype=np.uint8)
+    off = np.array([0, 1], dtype=np.int32)
+    c = M.grouped_gemm_ref(ones, unit, off, w, ws, np.array([1.0]))
+    assert c[0].tolist() == [0.0, 0.0, 6.0, 0.0]
+    w[0] = 0x22
+    c = M.grouped_gemm_ref(ones, unit, off, w, ws, np.array([0.25]))
+    assert np.all(c == 0.25 * K)
+
+
+def test_silu_mul_closed_form():
+    c1 = np.array([[0.0, 1.0, 50.0, -50.0, 2.0, 3.0, 1.0, -1.0]])
+    h = M.silu_mul(c1, 4)
+    assert h[0, 0] == 0.0
+    assert h[0, 1] == pytest.approx(3.0 / (1 + math.exp(-1.0)), rel=1e-15)
+    assert h[0, 2] == pytest.approx(50.0, rel=1e-15)
+    assert abs(h[0, 3]) < 1e-19
+
+
+def test_combine_closed_form():
+    T, k, H = 3, 2, 4
+    c2 = np.arange(T * k * H, dtype=np.float64).reshape(T * k, H)
+    inv = np.array([5, 0, 1, 2, 3, 4], dtype=np.int32)
+    w = np.array([[1.0, 0.0], [0.25, 0.75], [0.5, 0.5]])
+    res = np.ones((T, H), dtype=np.float32)
+    out = M.combine_ref(c2, w, inv, T, k, res)
+    assert out[0].tolist() == (c2[5] + 1).tolist()
+    assert out[1].tolist() == (0.25 * c2[1] + 0.75 * c2[2] + 1).tolist()
+
+
+# --- calibration, weights, layer --------------------------------------------
+
+def test_calibration_leaves_unrouted_expert_unwritten():
+    rng = np.random.default_rng(6)
+    E, k, H = 4, 2, 32
+    x = S.f32_to_bf16_bits(rng.standard_normal((10, H)).astype(np.float32))
+    logits = rng.standard_normal((10, E)).astype(np.float32)
+    logits[:, 3] = -100.0                     # expert 3 never selected
+    s13, wr = M.calibrate_input_scale(x, logits, k, E)
+    assert wr.tolist() == [1, 1, 1, 0] and np.isnan(s13[3])
+    ok, gs, st = M.validate_scales(s13, wr)
+    assert not ok and st[3] == M.SLOT_UNWRITTEN
+    ids, _ = M.route(logits, k)
+    t0 = np.nonzero((ids == 0).any(axis=1))[0]
+    assert s13[0] == np.float32(np.abs(S.bf16_bits_to_f32(x[t0])).max()) / np.float32(2688)
+
+
+def test_weight_quantisation_range():
+    rng = np.random.default_rng(11)
+    w = S.f32_to_bf16_bits((rng.standard_normal((8, 64)) * 0.02).astype(np.float32))
+    c, s, s2 = M.quantize_weight(w)
+    amax = np.abs(S.bf16_bits_to_f32(w)).max()
+    assert s2 == np.float32(amax) / np.float32(2688)
+    # the largest weight maps to the top of the combined range: E4M3 448, code 6
+    assert s.max() == 0x7E
+    deq = M.dequant_weight(c, s, s2)
+    x = S.bf16_bits_to_f32(w).astype(np.float64)
+    # per block: E2M1's widest gap (4 -> 6) bounds the element error by one
+    # block-scale unit, the E4M3 rounding of that unit by 1/16, and the
+    # resulting clamp by amax/16: |err| <= amax_b * (1.0625/6 + 1/16) < amax_b/4
+    err = np.abs(deq - x).reshape(8, 4, 16)
+    amax_b = np.abs(x).reshape(8, 4, 16).max(axis=-1, keepdims=True)
+    assert np.all(err <= amax_b / 4)
+
+
+def test_tiny_layer_end_to_end_properties():
+    w = S.WORKLOADS["tiny"]
+    w13, w2 = S.expert_weights(w)
+    xc, lc = S.calibration_batch(w)
+    layer = M.prepare_layer(w13, w2, xc, lc, w.k)
+    assert layer.written13.all() and layer.written2.all()
+    x = S.activations(w)
+    logits = S.router_logits(w)
+    r = M.layer_forward(layer, x, logits, w.k)
+    # the quantised layer tracks the unquantised fp64 layer
+    xf = S.bf16_bits_to_f32(x).astype(np.float64)
+    ref = np.zeros((w.T, w.H))
+    for t in range(w.T):
+        for j in range(w.k):
+            e = r["ids"][t, j]
+            W13 = M.dequant_weight(layer.w13c[e], layer.w13s[e], layer.w13s2[e])
+            W2 = M.dequant_weight(layer.w2c[e], layer.w2s[e], layer.w2s2[e])
+            h = M.silu_mul((xf[t] @ W13.T)[None, :], w.I)
+            ref[t] += r["w"][t, j] * (h @ W2.T)[0]
+    rel = np.linalg.norm(r["out_f64"] - ref) / np.linalg.norm(ref)
+    assert rel < 0.25, rel           # W4A4 quantisation noise, not a bug
+    # and the output is the combine of its own C2 rows
+    again = M.combine_ref(r["c2"], r["w"], r["inv"], w.T, w.k)
+    assert np.array_equal(again, r["out_f64"])
+
+
+# --- workloads --------------------------------------------------------------
+
+def test_workload_shapes_and_determinism():
+    w = S.WORKLOADS["tiny"]
+    a = S.activations(w)
+    b = S.activations(w)
+    assert a.shape == (64, 256) and a.dtype == np.uint16 and np.array_equal(a, b)
+    w13, w2 = S.expert_weights(w)
+    assert w13.shape == (4, 256, 256) and w2.shape == (4, 256, 128)
+    w13b, _ = S.expert_weights(w, experts=[2])
+    assert np.array_equal(w13b[0], w13[2])
+    assert S.router_logits(w).shape == (64, 4)
+
+
+def test_outlier_channels_and_saturation_on_quantizer_workload():
+    w = S.WORKLOADS["quant"]
+    ch = S.outlier_channels(w)
+    assert ch.size == 28
+    x = S.activations(w, tokens=64)
+    xf = S.bf16_bits_to_f32(x)
+    assert np.abs(xf[:, ch]).mean() > 20 * np.abs(np.delete(xf, ch, axis=1)).mean()
+    xc, lc = S.calibration_batch(w)
+    s13, wr = M.calibrate_input_scale(xc, lc, w.k, w.E)
+    assert wr.all()
+    ok, gs, _ = M.validate_scales(s13, wr)
+    ids, _ = M.route(S.router_logits(w, tokens=64), w.k)
+    off, src, inv = M.permute(ids, w.E)
+    codes, sf = Q.quantize_experts(x[src // w.k], M.row_experts(off), gs)
+    # the outliers push both levels into saturation
+    assert np.count_nonzero(sf == 0x7E) > 0
+    nib = F.unpack_nibbles(codes)
+    assert np.count_nonzero((nib & 7) == 7) > 0
+
+
+def test_zipf_router_leaves_experts_without_tokens():
+    w = S.WORKLOADS["stack"]
+    for layer in [0, 17]:
+        logits = S.router_logits(w, layer=layer, tokens=8192)
+        ids, _ = M.route(logits, w.k)
+        counts = np.bincount(ids.reshape(-1), minlength=w.E)
+        assert np.count_nonzero(counts == 0) >= 1
+        assert counts.max() > 20 * np.median(counts[counts > 0]) / 4
+
+
+def test_bias_router_is_skewed():
+    w = S.WORKLOADS["prefill"]
+    ids, _ = M.route(S.router_logits(w), w.k)
+    counts = np.bincount(ids.reshape(-1), minlength=w.E)
+    assert counts.max() > 4 * counts.mean() and counts.min() < counts.mean() / 4
+
+
+def test_bad_scale_slots_recipe():
+    slots = S.bad_scale_slots(S.WORKLOADS["stack"])
+    assert len(slots) == 3 and len({e for _, e, _ in slots}) == 3
+    assert {k for _, _, k in slots} == {"nan", "unwritten_garbage", "unwritten_neg"}
