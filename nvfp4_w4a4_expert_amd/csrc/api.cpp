@@ -1,0 +1,260 @@
+// C ABI of libnvfp4moe.so: argument checking, the load-time scale check,
+// workspace layout and the launch sequence of one MoE layer.
+#include <math.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#define NVFP4_BUILDING_LIBRARY 1
+#include "../../include/nvfp4_moe.h"
+#include "internal.h"
+
+namespace {
+
+using namespace nvfp4;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+nvfp4_status_t device_status(hipError_t e) {
+  return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_DEVICE;
+}
+
+// Byte layout of the forward pass's workspace.
+struct Layout {
+  size_t ids, wts, offsets, src_pair, inv, a1c, a1s, a2c, a2s, c2, total;
+};
+
+Layout layout(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I) {
+  const int64_t P = T * k;
+  Layout L;
+  size_t o = 0;
+  L.ids = o;      o = align_up(o + (size_t)P * 4);
+  L.wts = o;      o = align_up(o + (size_t)P * 4);
+  L.offsets = o;  o = align_up(o + (size_t)(E + 1) * 4);
+  L.src_pair = o; o = align_up(o + (size_t)P * 4);
+  L.inv = o;      o = align_up(o + (size_t)P * 4);
+  L.a1c = o;      o = align_up(o + (size_t)P * (H / 2));
+  L.a1s = o;      o = align_up(o + (size_t)P * (H / 16));
+  L.a2c = o;      o = align_up(o + (size_t)P * (I / 2));
+  L.a2s = o;      o = align_up(o + (size_t)P * (I / 16));
+  L.c2 = o;       o = align_up(o + (size_t)P * H * 4);
+  L.total = o;
+  return L;
+}
+
+nvfp4_status_t check_weights(const nvfp4_moe_weights_t* w) {
+  if (!w || !w->w13 || !w->w13_sf || !w->w13_scale2 || !w->w2 || !w->w2_sf || !w->w2_scale2 ||
+      !w->w13_input_scale || !w->w2_input_scale || !w->a1_gscale || !w->a2_gscale)
+    return NVFP4_ERR_INVALID_ARG;
+  if (w->num_experts <= 0 || w->hidden <= 0 || w->inter <= 0) return NVFP4_ERR_INVALID_ARG;
+  if (w->hidden % 16 || w->inter % 16) return NVFP4_ERR_INVALID_ARG;
+  if (!aligned(w->w13, 16) || !aligned(w->w2, 16)) return NVFP4_ERR_INVALID_ARG;
+  if (w->num_experts > 1024) return NVFP4_ERR_UNSUPPORTED;
+  if (w->hidden % 128 || w->inter % 64) return NVFP4_ERR_UNSUPPORTED;
+  return NVFP4_OK;
+}
+
+hipError_t copy_async(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  if (!dst || bytes == 0) return hipSuccess;
+  return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+NVFP4_API const char* nvfp4_status_string(nvfp4_status_t status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_INVALID_ARG: return "invalid argument";
+    case NVFP4_ERR_BAD_SCALE: return "per-expert input scale failed the load-time check";
+    case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case NVFP4_ERR_DEVICE: return "HIP runtime error";
+    case NVFP4_ERR_UNSUPPORTED: return "shape not supported by the built kernels";
+  }
+  return "unknown status";
+}
+
+NVFP4_API int32_t nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+NVFP4_API nvfp4_status_t nvfp4_validate_scales(const float* input_scale, const uint8_t* written,
+                                               int32_t num_experts, float* gscale_out,
+                                               int32_t* slot_status, int32_t* num_bad) {
+  if (!input_scale || num_experts <= 0) return NVFP4_ERR_INVALID_ARG;
+  int32_t bad = 0;
+  for (int32_t e = 0; e < num_experts; ++e) {
+    // read the bits, so a signalling pattern is never used as a float operand
+    uint32_t bits;
+    memcpy(&bits, input_scale + e, 4);
+    const uint32_t mag = bits & 0x7FFFFFFFu;
+    int32_t st = NVFP4_SLOT_OK;
+    if (written && !written[e]) st = NVFP4_SLOT_UNWRITTEN;
+    else if (mag > 0x7F800000u) st = NVFP4_SLOT_NAN;
+    else if (mag == 0x7F800000u) st = NVFP4_SLOT_INF;
+    else if ((bits >> 31) || mag == 0) st = NVFP4_SLOT_NONPOSITIVE;
+    else {
+      volatile float x = input_scale[e];
+      const float r = 1.0f / x;
+      if (!isfinite(r)) st = NVFP4_SLOT_RECIP_OVERFLOW;
+    }
+    if (slot_status) slot_status[e] = st;
+    bad += st != NVFP4_SLOT_OK;
+  }
+  if (num_bad) *num_bad = bad;
+  if (bad) return NVFP4_ERR_BAD_SCALE;
+  if (gscale_out)
+    for (int32_t e = 0; e < num_experts; ++e) gscale_out[e] = 1.0f / input_scale[e];
+  return NVFP4_OK;
+}
+
+NVFP4_API nvfp4_status_t nvfp4_quantize_experts(const void* x_bf16, int64_t ldx, int32_t num_rows,
+                                                int32_t K, int32_t topk, const int32_t* expert_idx,
+                                                const int32_t* dst_row, int32_t num_experts,
+                                                const float* gscale, uint8_t* codes, uint8_t* sf,
+                                                int32_t num_dst_rows, nvfp4_stream_t stream) {
+  if (num_rows < 0 || K <= 0 || K % 16 || topk < 1 || num_experts < 1 || num_dst_rows < 0 ||
+      ldx < K || ldx % 8)
+    return NVFP4_ERR_INVALID_ARG;
+  if (num_rows == 0) return NVFP4_OK;
+  if (!x_bf16 || !codes || !sf || !aligned(x_bf16, 16) || !aligned(codes, 8))
+    return NVFP4_ERR_INVALID_ARG;
+  return device_status(launch_quantize(static_cast<const uint16_t*>(x_bf16), ldx, num_rows, K,
+                                       topk, expert_idx, dst_row, num_experts, gscale, codes, sf,
+                                       num_dst_rows, static_cast<hipStream_t>(stream)));
+}
+
+NVFP4_API nvfp4_status_t nvfp4_route_topk(const float* logits, int32_t num_tokens,
+                                          int32_t num_experts, int32_t k, int32_t* ids,
+                                          float* weights, nvfp4_stream_t stream) {
+  if (num_tokens < 0 || num_experts < 1 || k < 1 || k > num_experts) return NVFP4_ERR_INVALID_ARG;
+  if (num_experts > 1024 || k > 32) return NVFP4_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return NVFP4_OK;
+  if (!logits || !ids || !weights) return NVFP4_ERR_INVALID_ARG;
+  return device_status(launch_route(logits, num_tokens, num_experts, k, ids, weights,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+NVFP4_API nvfp4_status_t nvfp4_permute(const int32_t* ids, int32_t num_tokens, int32_t k,
+                                       int32_t num_experts, int32_t* expert_offsets,
+                                       int32_t* src_pair, int32_t* inv_pair,
+                                       nvfp4_stream_t stream) {
+  if (num_tokens < 0 || k < 1 || num_experts < 1) return NVFP4_ERR_INVALID_ARG;
+  if (!expert_offsets) return NVFP4_ERR_INVALID_ARG;
+  if (num_tokens > 0 && (!ids || !src_pair || !inv_pair)) return NVFP4_ERR_INVALID_ARG;
+  if ((int64_t)num_tokens * k > 0x7FFFFFFF) return NVFP4_ERR_UNSUPPORTED;
+  return device_status(launch_permute(ids, num_tokens * k, num_experts, expert_offsets, src_pair,
+                                      inv_pair, static_cast<hipStream_t>(stream)));
+}
+
+NVFP4_API nvfp4_status_t nvfp4_expert_absmax(const void* x_bf16, int64_t ldx, int32_t K,
+                                             const int32_t* src, int32_t src_div,
+                                             const int32_t* expert_offsets, int32_t num_experts,
+                                             int32_t num_rows, float* amax_out,
+                                             nvfp4_stream_t stream) {
+  if (K <= 0 || K % 8 || ldx < K || ldx % 8 || src_div < 1 || num_experts < 1 || num_rows < 0)
+    return NVFP4_ERR_INVALID_ARG;
+  if (!expert_offsets || !amax_out) return NVFP4_ERR_INVALID_ARG;
+  if (num_rows > 0 && (!x_bf16 || !aligned(x_bf16, 16))) return NVFP4_ERR_INVALID_ARG;
+  return device_status(launch_absmax(static_cast<const uint16_t*>(x_bf16), ldx, K, src, src_div,
+                                     expert_offsets, num_experts, num_rows, amax_out,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+NVFP4_API nvfp4_status_t nvfp4_moe_workspace_size(int32_t num_tokens, int32_t k,
+                                                  const nvfp4_moe_weights_t* w, size_t* bytes) {
+  if (!bytes || !w || num_tokens < 0 || k < 1) return NVFP4_ERR_INVALID_ARG;
+  if (w->num_experts <= 0 || w->hidden <= 0 || w->inter <= 0) return NVFP4_ERR_INVALID_ARG;
+  *bytes = layout(num_tokens, k, w->num_experts, w->hidden, w->inter).total;
+  return NVFP4_OK;
+}
+
+NVFP4_API nvfp4_status_t nvfp4_moe_forward(const nvfp4_moe_weights_t* w, const void* x_bf16,
+                                           const float* router_logits, int32_t num_tokens,
+                                           int32_t k, const void* residual_bf16, void* out_bf16,
+                                           void* workspace, size_t workspace_bytes,
+                                           const nvfp4_moe_debug_t* debug, nvfp4_stream_t stream) {
+  nvfp4_status_t st = check_weights(w);
+  if (st != NVFP4_OK) return st;
+  const int32_t E = w->num_experts, H = w->hidden, I = w->inter;
+  if (num_tokens < 0 || k < 1 || k > E) return NVFP4_ERR_INVALID_ARG;
+  if (k > 32) return NVFP4_ERR_UNSUPPORTED;
+  if ((int64_t)num_tokens * k > (1 << 30)) return NVFP4_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return NVFP4_OK;
+  if (!x_bf16 || !router_logits || !out_bf16) return NVFP4_ERR_INVALID_ARG;
+  if (!aligned(x_bf16, 16) || !aligned(out_bf16, 16) ||
+      (residual_bf16 && !aligned(residual_bf16, 16)))
+    return NVFP4_ERR_INVALID_ARG;
+  const Layout L = layout(num_tokens, k, E, H, I);
+  if (!workspace || workspace_bytes < L.total || !aligned(workspace, kAlign))
+    return NVFP4_ERR_WORKSPACE;
+
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t T = num_tokens, P = T * k;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
+  float* wts = reinterpret_cast<float*>(ws + L.wts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* src_pair = reinterpret_cast<int32_t*>(ws + L.src_pair);
+  int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
+  uint8_t* a1c = reinterpret_cast<uint8_t*>(ws + L.a1c);
+  uint8_t* a1s = reinterpret_cast<uint8_t*>(ws + L.a1s);
+  uint8_t* a2c = reinterpret_cast<uint8_t*>(ws + L.a2c);
+  uint8_t* a2s = reinterpret_cast<uint8_t*>(ws + L.a2s);
+  float* c2 = reinterpret_cast<float*>(ws + L.c2);
+
+  void** ev = debug ? debug->stage_events : nullptr;
+  auto mark = [&](int i) -> hipError_t {
+    return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
+  };
+  hipError_t err = mark(0);
+  if (err == hipSuccess) err = launch_route(router_logits, T, E, k, ids, wts, s);
+  if (err == hipSuccess) err = mark(1);
+  if (err == hipSuccess) err = launch_permute(ids, P, E, offsets, src_pair, inv, s);
+  if (err == hipSuccess) err = mark(2);
+  if (err == hipSuccess)
+    err = launch_quantize(static_cast<const uint16_t*>(x_bf16), H, T, H, k, ids, inv, E,
+                          w->a1_gscale, a1c, a1s, P, s);
+  if (err == hipSuccess) err = mark(3);
+  if (err == hipSuccess) {
+    Gemm1Args g1;
+    g1.a_codes = a1c; g1.a_sf = a1s; g1.w_codes = w->w13; g1.w_sf = w->w13_sf;
+    g1.in_scale = w->w13_input_scale; g1.w_scale2 = w->w13_scale2; g1.out_gscale = w->a2_gscale;
+    g1.offsets = offsets; g1.out_codes = a2c; g1.out_sf = a2s;
+    g1.c1_dbg = debug ? debug->c1 : nullptr;
+    g1.h_dbg = debug ? debug->h : nullptr;
+    g1.P = P; g1.E = E; g1.H = H; g1.I = I;
+    err = launch_gemm1(g1, s);
+  }
+  if (err == hipSuccess) err = mark(4);
+  if (err == hipSuccess) {
+    Gemm2Args g2;
+    g2.a_codes = a2c; g2.a_sf = a2s; g2.w_codes = w->w2; g2.w_sf = w->w2_sf;
+    g2.in_scale = w->w2_input_scale; g2.w_scale2 = w->w2_scale2; g2.offsets = offsets;
+    g2.out = c2; g2.P = P; g2.E = E; g2.H = H; g2.I = I;
+    err = launch_gemm2(g2, s);
+  }
+  if (err == hipSuccess) err = mark(5);
+  if (err == hipSuccess)
+    err = launch_combine(c2, wts, inv, T, k, H, static_cast<const uint16_t*>(residual_bf16),
+                         static_cast<uint16_t*>(out_bf16), s);
+  if (err == hipSuccess) err = mark(6);
+  if (err == hipSuccess && debug) {
+    err = copy_async(debug->topk_ids, ids, (size_t)P * 4, s);
+    if (err == hipSuccess) err = copy_async(debug->topk_weights, wts, (size_t)P * 4, s);
+    if (err == hipSuccess) err = copy_async(debug->expert_offsets, offsets, (size_t)(E + 1) * 4, s);
+    if (err == hipSuccess) err = copy_async(debug->src_pair, src_pair, (size_t)P * 4, s);
+    if (err == hipSuccess) err = copy_async(debug->inv_pair, inv, (size_t)P * 4, s);
+    if (err == hipSuccess) err = copy_async(debug->a1_codes, a1c, (size_t)P * (H / 2), s);
+    if (err == hipSuccess) err = copy_async(debug->a1_sf, a1s, (size_t)P * (H / 16), s);
+    if (err == hipSuccess) err = copy_async(debug->a2_codes, a2c, (size_t)P * (I / 2), s);
+    if (err == hipSuccess) err = copy_async(debug->a2_sf, a2s, (size_t)P * (I / 16), s);
+    if (err == hipSuccess) err = copy_async(debug->c2, c2, (size_t)P * H * 4, s);
+  }
+  return device_status(err);
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// Internal launchers shared between the kernel translation units and the
+// C-ABI layer.  Not exported from the shared library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+hipError_t launch_quantize(const uint16_t* x, int64_t ldx, int32_t num_rows, int32_t K,
+                           int32_t topk, const int32_t* expert_idx, const int32_t* dst_row,
+                           int32_t num_experts, const float* gscale, uint8_t* codes, uint8_t* sf,
+                           int32_t num_dst_rows, hipStream_t stream);
+
+hipError_t launch_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* ids,
+                        float* weights, hipStream_t stream);
+
+hipError_t launch_permute(const int32_t* ids, int32_t P, int32_t E, int32_t* offsets,
+                          int32_t* src_pair, int32_t* inv, hipStream_t stream);
+
+hipError_t launch_absmax(const uint16_t* x, int64_t ldx, int32_t K, const int32_t* src,
+                         int32_t src_div, const int32_t* offsets, int32_t E, int32_t num_rows,
+                         float* amax, hipStream_t stream);
+
+struct Gemm1Args {
+  const uint8_t* a_codes;   // [P, H/2]
+  const uint8_t* a_sf;      // [P, H/16]
+  const uint8_t* w_codes;   // [E, 2I, H/2]
+  const uint8_t* w_sf;      // [E, 2I, H/16]
+  const float* in_scale;    // [E] w13_input_scale
+  const float* w_scale2;    // [E] w13_scale2
+  const float* out_gscale;  // [E] a2_gscale (requant of h)
+  const int32_t* offsets;   // [E+1]
+  uint8_t* out_codes;       // [P, I/2]
+  uint8_t* out_sf;          // [P, I/16]
+  float* c1_dbg;            // [P, 2I] or null
+  uint16_t* h_dbg;          // [P, I] or null
+  int32_t P, E, H, I;
+};
+
+struct Gemm2Args {
+  const uint8_t* a_codes;   // [P, I/2]
+  const uint8_t* a_sf;      // [P, I/16]
+  const uint8_t* w_codes;   // [E, H, I/2]
+  const uint8_t* w_sf;      // [E, H, I/16]
+  const float* in_scale;    // [E] w2_input_scale
+  const float* w_scale2;    // [E] w2_scale2
+  const int32_t* offsets;   // [E+1]
+  float* out;               // [P, H]
+  int32_t P, E, H, I;
+};
+
+hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream);
+hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream);
+
+hipError_t launch_combine(const float* c2, const float* w, const int32_t* inv, int32_t T,
+                          int32_t k, int32_t H, const uint16_t* residual, uint16_t* out,
+                          hipStream_t stream);
+
+}  // namespace nvfp4

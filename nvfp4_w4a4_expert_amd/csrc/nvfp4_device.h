@@ -1,0 +1,131 @@
+// Device-side NVFP4 helpers for gfx950: bf16 unpacking, OCP E4M3 scale
+// encode/decode, E2M1 encode, and the 16-element block quantiser.
+//
+// Format facts (page 3, "Gemma 4 NVFP4 MoE 空输出", "NVFP4" section): an
+// NVFP4 value is an E2M1 code (1 sign, 2 exponent, 1 mantissa bit; largest
+// magnitude 6) times an E4M3 block scale shared by 16 consecutive elements
+// (largest finite 448) times an FP32 global scale.  Encoding to E2M1 rounds
+// to nearest with ties to even and saturates to the largest finite value.
+// The activation quantiser (same section, runtime-order figure) takes the
+// expert's SFScaleVal (the reciprocal of its FP32 input_scale), the block's
+// absolute maximum and the E2M1 maximum 6 to form the block scale, rounds it
+// to E4M3, normalises the 16 values by it and rounds them to E2M1.
+//
+// Every fp32 operation below is a single IEEE operation rounded to nearest
+// even (no contraction, correctly rounded division, fp32 denormals kept), so
+// the produced codes are a deterministic function of the inputs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kE2M1Max = 6.0f;
+constexpr float kE4M3Max = 448.0f;
+constexpr float kFltMax = 3.40282346638528859812e+38f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Non-negative fp32 (or +inf) -> E4M3 code 0x00..0x7E: nearest finite value,
+// ties to the even code, saturating at 448 (0x7E; 0x7F is NaN in E4M3).
+__device__ __forceinline__ uint32_t e4m3_encode(float s) {
+  if (!(s < kE4M3Max)) return 0x7Eu;
+  const uint32_t u = __float_as_uint(s);
+  const int e = (int)(u >> 23) - 127;              // exponent of s (-127 for 0 / fp32 denormals)
+  if (e < -6) {
+    // E4M3 subnormal range: multiples of 2^-9 (code == multiple, 8 == 2^-6).
+    // s * 512 is exact (power-of-two scaling of a value far from overflow);
+    // rintf rounds to nearest even.
+    return (uint32_t)__builtin_rintf(s * 512.0f);
+  }
+  const uint32_t mant = u & 0x7FFFFFu;
+  uint32_t code = ((uint32_t)(e + 7) << 3) | (mant >> 20);
+  const uint32_t rem = mant & 0xFFFFFu;               // dropped 20 mantissa bits
+  code += (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) ? 1u : 0u;
+  return code;                                       // s < 448 keeps this <= 0x7E
+}
+
+// E4M3 code (non-negative, finite) -> fp32 value, exact.
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  if (e == 0) return (float)m * 0.001953125f;         // m * 2^-9
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// |v| -> E2M1 magnitude code, nearest with ties to the even code, saturating.
+// Midpoints between the magnitudes {0,.5,1,1.5,2,3,4,6}: .25 .75 1.25 1.75
+// 2.5 3.5 5; a midpoint goes to the neighbour whose code is even.
+__device__ __forceinline__ uint32_t e2m1_mag(float a) {
+  return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+         (uint32_t)(a > 5.0f);
+}
+
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return ((u >> 28) & 8u) | e2m1_mag(__uint_as_float(u & 0x7FFFFFFFu));
+}
+
+// Block scale for one (block, expert): from amax/6 (computed once per block)
+// and the expert's SFScaleVal gs.  Returns the E4M3 code and the multiplier
+// that normalises the block's elements.
+struct BlockScale {
+  uint32_t sf;
+  float inv;
+};
+
+__device__ __forceinline__ BlockScale block_scale(float amax_over_6, float gs) {
+#pragma clang fp contract(off)
+  BlockScale r;
+  const float s = gs * amax_over_6;
+  r.sf = e4m3_encode(s);
+  const float sv = e4m3_decode(r.sf);
+  r.inv = (sv == 0.0f) ? 0.0f : fminf(gs / sv, kFltMax);
+  return r;
+}
+
+// Encode 8 consecutive elements (already multiplied by nothing) into one
+// 32-bit word of packed codes: element i goes to bits [4i, 4i+4).
+__device__ __forceinline__ uint32_t encode8(const float* x, float inv) {
+#pragma clang fp contract(off)
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w |= e2m1_code(x[i] * inv) << (4 * i);
+  return w;
+}
+
+// max |x_i| over 16 values (exact).
+__device__ __forceinline__ float absmax16(const float* x) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(x[i]));
+  return m;
+}
+
+// Unpack 8 bf16 held in a 16-byte vector into floats.
+__device__ __forceinline__ void unpack_bf16x8(const u32x4& u, float* x) {
+  x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x);
+  x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
+  x[4] = bf16_lo(u.z); x[5] = bf16_hi(u.z);
+  x[6] = bf16_lo(u.w); x[7] = bf16_hi(u.w);
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4& v, float* x) {
+  x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+  x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+  x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+  x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+}
+
+}  // namespace nvfp4

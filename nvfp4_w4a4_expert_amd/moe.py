@@ -1,0 +1,204 @@
+"""One NVFP4 W4A4 routed-expert MoE layer on the GPU.
+
+``NVFP4MoELayer`` holds one layer's checkpoint fields on the device and runs
+``nvfp4_moe_forward``.  Construction performs the load-time scale check
+(``nvfp4_validate_scales``) on the host before any reciprocal is kept: a
+layer whose per-expert input scales are unwritten, NaN, infinite,
+non-positive or too small to invert is rejected with :class:`BadScaleError`
+and nothing is uploaded.
+
+``quantize_expert_weights`` and ``calibrate_layer`` produce a layer from bf16
+weights with the library's own kernels (static weight quantisation and
+activation-scale calibration); they stand in for an offline exporter.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib
+
+NVFP4_RANGE = np.float32(6.0 * 448.0)   # E2M1 max x E4M3 max
+
+
+class BadScaleError(ValueError):
+    """Per-expert activation scales failed the load-time check."""
+
+    def __init__(self, projection: str, slot_status: np.ndarray):
+        self.projection = projection
+        self.slot_status = slot_status
+        self.bad_slots = [int(e) for e in np.nonzero(slot_status != _lib.SLOT_OK)[0]]
+        super().__init__(f"{projection}_input_scale: {len(self.bad_slots)} bad expert slot(s) "
+                         f"{self.bad_slots}")
+
+
+def _dev_u8(a, device):
+    return torch.as_tensor(np.ascontiguousarray(a, dtype=np.uint8)).to(device)
+
+
+def _dev_f32(a, device):
+    return torch.as_tensor(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def bf16_tensor(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    """uint16 bf16 bit patterns -> torch.bfloat16 tensor on `device`."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
+    return torch.from_numpy(b).to(device).view(torch.bfloat16)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class NVFP4MoELayer:
+    """Device-resident NVFP4 MoE layer.
+
+    Weight tensors may be numpy arrays (uploaded) or device tensors (used in
+    place): w13 [E, 2I, H/2] u8, w13_sf [E, 2I, H/16] u8, w13_scale2 [E] f32,
+    w2 [E, H, I/2] u8, w2_sf [E, H, I/16] u8, w2_scale2 [E] f32.  The input
+    scales and `written` masks are host arrays; they are checked first.
+    """
+
+    def __init__(self, w13, w13_sf, w13_scale2, w2, w2_sf, w2_scale2,
+                 w13_input_scale, w2_input_scale, written13=None, written2=None,
+                 device="cuda"):
+        s13 = np.ascontiguousarray(w13_input_scale, dtype=np.float32)
+        s2 = np.ascontiguousarray(w2_input_scale, dtype=np.float32)
+        st, gs1, slots, _ = _lib.validate_scales(s13, written13)
+        if st != _lib.OK:
+            raise BadScaleError("w13", slots)
+        st, gs2, slots, _ = _lib.validate_scales(s2, written2)
+        if st != _lib.OK:
+            raise BadScaleError("w2", slots)
+        up8 = (lambda a: a if isinstance(a, torch.Tensor) else _dev_u8(a, device))
+        up32 = (lambda a: a if isinstance(a, torch.Tensor) else _dev_f32(a, device))
+        self.w13, self.w13_sf, self.w13_scale2 = up8(w13), up8(w13_sf), up32(w13_scale2)
+        self.w2, self.w2_sf, self.w2_scale2 = up8(w2), up8(w2_sf), up32(w2_scale2)
+        self.w13_input_scale = _dev_f32(s13, device)
+        self.w2_input_scale = _dev_f32(s2, device)
+        self.a1_gscale = _dev_f32(gs1, device)
+        self.a2_gscale = _dev_f32(gs2, device)
+        self.E = int(self.w13.shape[0])
+        self.I = int(self.w13.shape[1]) // 2
+        self.H = int(self.w13.shape[2]) * 2
+        self.device = device
+        self._ws = None
+
+    def weights(self) -> _lib.MoEWeights:
+        return _lib.MoEWeights(
+            self.w13.data_ptr(), self.w13_sf.data_ptr(), self.w13_scale2.data_ptr(),
+            self.w2.data_ptr(), self.w2_sf.data_ptr(), self.w2_scale2.data_ptr(),
+            self.w13_input_scale.data_ptr(), self.w2_input_scale.data_ptr(),
+            self.a1_gscale.data_ptr(), self.a2_gscale.data_ptr(), self.E, self.H, self.I)
+
+    def workspace(self, T: int, k: int) -> torch.Tensor:
+        n = _lib.moe_workspace_size(T, k, self.weights())
+        if self._ws is None or self._ws.numel() < n:
+            self._ws = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def forward(self, x: torch.Tensor, logits: torch.Tensor, k: int,
+                residual: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                debug: bool = False, stream=None):
+        """x bf16 [T, H], logits fp32 [T, E] -> out bf16 [T, H] (and a dict of
+        intermediates when debug=True)."""
+        T = int(x.shape[0])
+        if out is None:
+            out = torch.empty_like(x)
+        ws = self.workspace(T, k)
+        w = self.weights()
+        dbg = None
+        bufs = None
+        if debug:
+            P, H, I, E = T * k, self.H, self.I, self.E
+            dev = self.device
+            bufs = dict(
+                topk_ids=torch.empty((T, k), dtype=torch.int32, device=dev),
+                topk_weights=torch.empty((T, k), dtype=torch.float32, device=dev),
+                expert_offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                src_pair=torch.empty(P, dtype=torch.int32, device=dev),
+                inv_pair=torch.empty(P, dtype=torch.int32, device=dev),
+                a1_codes=torch.empty((P, H // 2), dtype=torch.uint8, device=dev),
+                a1_sf=torch.empty((P, H // 16), dtype=torch.uint8, device=dev),
+                c1=torch.empty((P, 2 * I), dtype=torch.float32, device=dev),
+                h=torch.empty((P, I), dtype=torch.int16, device=dev),
+                a2_codes=torch.empty((P, I // 2), dtype=torch.uint8, device=dev),
+                a2_sf=torch.empty((P, I // 16), dtype=torch.uint8, device=dev),
+                c2=torch.empty((P, H), dtype=torch.float32, device=dev),
+            )
+            dbg = _lib.MoEDebug(**{name: t.data_ptr() for name, t in bufs.items()})
+        _lib.moe_forward(w, x, logits, T, k, residual, out, ws, ws.numel(), dbg, stream)
+        return (out, bufs) if debug else out
+
+
+# --- producing a layer with the library's kernels ----------------------------
+
+def quantize_expert_weights(w: torch.Tensor, stream=None):
+    """Static NVFP4 quantisation of bf16 expert weights [E, N, K] on the GPU:
+    weight_scale_2[e] = fl32(max|W[e]| / 2688), SFScaleVal = fl32(1 / that),
+    then the per-expert quantiser.  Returns (codes, sf, scale2) tensors."""
+    E, N, K = (int(s) for s in w.shape)
+    dev = w.device
+    flat = w.reshape(E * N, K)
+    offsets = torch.arange(0, E * N + 1, N, dtype=torch.int32, device=dev)
+    amax = torch.empty(E, dtype=torch.float32, device=dev)
+    _lib.expert_absmax(flat, K, K, None, 1, offsets, E, E * N, amax, stream)
+    scale2 = (amax.cpu().numpy().astype(np.float32) / NVFP4_RANGE).astype(np.float32)
+    st, gs, slots, _ = _lib.validate_scales(scale2)
+    if st != _lib.OK:
+        raise BadScaleError("weight_scale_2", slots)
+    expert_of_row = torch.arange(E, dtype=torch.int32, device=dev).repeat_interleave(N)
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev)
+    sf = torch.empty((E, N, K // 16), dtype=torch.uint8, device=dev)
+    _lib.quantize_experts(flat, K, E * N, K, 1, expert_of_row, None, E,
+                          torch.from_numpy(gs).to(dev), codes, sf, E * N, stream)
+    return codes, sf, torch.from_numpy(scale2).to(dev)
+
+
+@dataclass
+class Calibration:
+    w13_input_scale: np.ndarray
+    w2_input_scale: np.ndarray
+    written13: np.ndarray
+    written2: np.ndarray
+
+
+def calibrate_layer(w13c, w13s, w13s2, w2c, w2s, w2s2, x_cal: torch.Tensor,
+                    logits_cal: torch.Tensor, k: int) -> Calibration:
+    """Per-expert activation scales from a calibration batch, with the
+    library's kernels: w13_input_scale = fl32(amax|x| / 2688) over the rows
+    routed to each expert; w2_input_scale = fl32(amax|h| / 2688) over the same
+    rows, where h is the layer's own SiLU(gate)*up (which does not depend on
+    the a2 scale).  Experts without calibration rows stay unwritten."""
+    dev = x_cal.device
+    Tc, H = (int(s) for s in x_cal.shape)
+    E = int(w13c.shape[0])
+    I = int(w13c.shape[1]) // 2
+    P = Tc * k
+    ids = torch.empty((Tc, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((Tc, k), dtype=torch.float32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    src = torch.empty(P, dtype=torch.int32, device=dev)
+    inv = torch.empty(P, dtype=torch.int32, device=dev)
+    _lib.route_topk(logits_cal, Tc, E, k, ids, wts)
+    _lib.permute(ids, Tc, k, E, offsets, src, inv)
+    amax_x = torch.empty(E, dtype=torch.float32, device=dev)
+    _lib.expert_absmax(x_cal, H, H, src, k, offsets, E, P, amax_x)
+    counts = np.diff(offsets.cpu().numpy())
+    written = (counts > 0).astype(np.uint8)
+    s13 = (amax_x.cpu().numpy() / NVFP4_RANGE).astype(np.float32)
+    s13[written == 0] = np.nan
+    # h does not depend on a2_gscale: run the layer with placeholder unit
+    # a2 scales, restricted to the written slots, and read h back.
+    ones = np.ones(E, dtype=np.float32)
+    s13_run = np.where(written == 1, s13, np.float32(1.0)).astype(np.float32)
+    layer = NVFP4MoELayer(w13c, w13s, w13s2, w2c, w2s, w2s2, s13_run, ones, device=dev)
+    _, dbg = layer.forward(x_cal, logits_cal, k, debug=True)
+    amax_h = torch.empty(E, dtype=torch.float32, device=dev)
+    _lib.expert_absmax(dbg["h"], I, I, None, 1, dbg["expert_offsets"], E, P, amax_h)
+    s2 = (amax_h.cpu().numpy() / NVFP4_RANGE).astype(np.float32)
+    s2[written == 0] = np.nan
+    return Calibration(s13, s2, written, written.copy())

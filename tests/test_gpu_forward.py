@@ -1,0 +1,142 @@
+"""GPU parity of nvfp4_moe_forward, stage by stage, on the five workloads'
+layers, plus edge cases (ragged tails, experts without rows, k = 1 and
+k = E, residual aliasing, determinism)."""
+import numpy as np
+import pytest
+
+import synthetic as S
+from oracle import moe as OM
+
+from gpu_helpers import check_layer_parity, oracle_layer, run_forward, device_layer
+
+pytestmark = pytest.mark.gpu
+
+
+def _report(label, m):
+    print(f"[{label}] C1 max {m['c1_max']:.2e}  h max {m['h_max']:.2e}  C2 max {m['c2_max']:.2e}  "
+          f"out max {m['out_max']:.2e} (median {m['out_median']:.2e})  e2e max {m['e2e_max']:.2e}  "
+          f"A2 bytes differing from oracle-own A2 {m['a2_byte_diffs_vs_own']}", flush=True)
+
+
+def test_tiny_layer():
+    w = S.WORKLOADS["tiny"]
+    layer = oracle_layer("tiny")
+    m = check_layer_parity(layer, S.activations(w), S.router_logits(w), w.k, label="tiny")
+    _report("tiny", m)
+
+
+def test_tiny_with_residual_ragged_and_empty_expert():
+    w = S.WORKLOADS["tiny"]
+    layer = oracle_layer("tiny")
+    rng = np.random.default_rng(5)
+    T = 70                                             # not a multiple of any tile
+    x = S.f32_to_bf16_bits(rng.standard_normal((T, w.H)).astype(np.float32))
+    res = S.f32_to_bf16_bits(rng.standard_normal((T, w.H)).astype(np.float32))
+    logits = rng.standard_normal((T, w.E)).astype(np.float32)
+    logits[:, 2] = -50.0                               # expert 2 receives no rows
+    m = check_layer_parity(layer, x, logits, w.k, residual_bits=res, label="tiny-res")
+    assert m["got"]["expert_offsets"][2] == m["got"]["expert_offsets"][3]
+    _report("tiny-res", m)
+
+
+@pytest.mark.parametrize("T,k", [(1, 1), (1, 4), (5, 4), (130, 1), (257, 3)])
+def test_tiny_k_and_token_counts(T, k):
+    w = S.WORKLOADS["tiny"]
+    layer = oracle_layer("tiny")
+    rng = np.random.default_rng(T * 10 + k)
+    x = S.f32_to_bf16_bits(rng.standard_normal((T, w.H)).astype(np.float32))
+    logits = rng.standard_normal((T, w.E)).astype(np.float32)
+    check_layer_parity(layer, x, logits, k, label=f"tiny T={T} k={k}")
+
+
+def test_zero_tokens_is_noop():
+    import torch
+    from nvfp4_w4a4_expert_amd import moe as M
+    layer = device_layer(oracle_layer("tiny"))
+    out = torch.full((1, 256), 3, dtype=torch.int16, device="cuda")
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    lg = torch.empty((0, 4), dtype=torch.float32, device="cuda")
+    from nvfp4_w4a4_expert_amd import _lib as L
+    L.moe_forward(layer.weights(), x, lg, 0, 2, None, out, None, 0)
+    torch.cuda.synchronize()
+    assert np.all(out.cpu().numpy() == 3)
+
+
+def test_determinism_and_residual_alias():
+    import torch
+    from nvfp4_w4a4_expert_amd import moe as M
+    w = S.WORKLOADS["tiny"]
+    dl = device_layer(oracle_layer("tiny"))
+    x = M.bf16_tensor(S.activations(w))
+    lg = torch.from_numpy(S.router_logits(w)).cuda()
+    a = dl.forward(x, lg, w.k)
+    b = dl.forward(x, lg, w.k)
+    res = M.bf16_tensor(S.activations(w))
+    c = dl.forward(x, lg, w.k, residual=res)
+    dl.forward(x, lg, w.k, residual=res, out=res)           # out aliases residual
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(c.view(torch.int16), res.view(torch.int16))
+
+
+@pytest.mark.timeout(900)
+def test_decode_layer():
+    w = S.WORKLOADS["decode"]
+    layer = oracle_layer("decode")
+    m = check_layer_parity(layer, S.activations(w), S.router_logits(w), w.k, label="decode")
+    _report("decode", m)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_layer():
+    w = S.WORKLOADS["prefill"]
+    layer = oracle_layer("prefill")
+    m = check_layer_parity(layer, S.activations(w), S.router_logits(w), w.k, label="prefill")
+    counts = np.diff(m["ref"]["offsets"])
+    assert counts.max() > 4 * counts.mean()            # non-uniform expert loads
+    _report("prefill", m)
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("layer_idx", [0, 29])
+def test_stack_layer(layer_idx):
+    """One layer of the 30-layer stack (its own weights, scales and Zipf
+    router) on a seeded N(0,1) input and residual of the stack's shape."""
+    w = S.WORKLOADS["stack"]
+    layer = oracle_layer("stack", layer_idx)
+    x = S.activations(w, layer=layer_idx)
+    logits = S.router_logits(w, layer=layer_idx)
+    m = check_layer_parity(layer, x, logits, w.k, residual_bits=x, label=f"stack L{layer_idx}")
+    assert np.count_nonzero(np.diff(m["ref"]["offsets"]) == 0) >= 1
+    _report(f"stack L{layer_idx}", m)
+
+
+def test_stack_bad_scales_rejected_at_load():
+    """The 30-layer stack's scale-validation case: three seeded corrupt slots
+    (NaN, unwritten with a valid-looking stale value, unwritten with -inf
+    bits) are named exactly and nothing is uploaded."""
+    from nvfp4_w4a4_expert_amd import moe as M
+    w = S.WORKLOADS["stack"]
+    s13 = np.full(w.E, 1.0 / 2688, dtype=np.float32)
+    s2 = np.full(w.E, 1.0 / 2688, dtype=np.float32)
+    wr13 = np.ones(w.E, dtype=np.uint8)
+    wr2 = np.ones(w.E, dtype=np.uint8)
+    for proj, e, kind in S.bad_scale_slots(w):
+        s, wr = (s13, wr13) if proj == "w13" else (s2, wr2)
+        if kind == "nan":
+            s[e] = np.nan
+        elif kind == "unwritten_garbage":
+            s[e] = np.float32(0.25)
+            wr[e] = 0
+        else:
+            s[e] = -np.inf
+            wr[e] = 0
+    bad13 = sorted(e for p, e, _ in S.bad_scale_slots(w) if p == "w13")
+    bad2 = sorted(e for p, e, _ in S.bad_scale_slots(w) if p == "w2")
+    with pytest.raises(M.BadScaleError) as ei:
+        M.NVFP4MoELayer(None, None, None, None, None, None, s13, s2, wr13, wr2, device="cuda")
+    assert ei.value.projection == "w13" and ei.value.bad_slots == bad13
+    s13_ok = np.full(w.E, 1.0 / 2688, dtype=np.float32)
+    with pytest.raises(M.BadScaleError) as ei:
+        M.NVFP4MoELayer(None, None, None, None, None, None, s13_ok, s2, None, wr2, device="cuda")
+    assert ei.value.projection == "w2" and ei.value.bad_slots == bad2

@@ -1,0 +1,128 @@
+"""GPU parity of nvfp4_quantize_experts against the oracle quantiser:
+packed E2M1 codes and E4M3 scales must be bit-exact."""
+import numpy as np
+import pytest
+
+import synthetic as S
+from oracle import formats as OF
+from oracle import moe as OM
+from oracle import quant as OQ
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    return torch
+
+
+def _gpu_quantize(x_bits, K, topk, expert_idx, dst_row, gscale, num_dst_rows):
+    torch = _torch()
+    from nvfp4_w4a4_expert_amd import _lib as L
+    from nvfp4_w4a4_expert_amd import moe as M
+    R = x_bits.shape[0]
+    x = M.bf16_tensor(x_bits)
+    ei = None if expert_idx is None else torch.from_numpy(np.ascontiguousarray(expert_idx, dtype=np.int32)).cuda()
+    dr = None if dst_row is None else torch.from_numpy(np.ascontiguousarray(dst_row, dtype=np.int32)).cuda()
+    gs = None if gscale is None else torch.from_numpy(np.ascontiguousarray(gscale, dtype=np.float32)).cuda()
+    E = 1 if gscale is None else len(gscale)
+    codes = torch.full((num_dst_rows, K // 2), 0xAB, dtype=torch.uint8, device="cuda")
+    sf = torch.full((num_dst_rows, K // 16), 0xCD, dtype=torch.uint8, device="cuda")
+    L.quantize_experts(x, x_bits.shape[1], R, K, topk, ei, dr, E, gs, codes, sf, num_dst_rows)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), sf.cpu().numpy()
+
+
+GS_SET = np.array([1.0, 1.0 / 3.0, 448.0 / 6.0, 2688.0, 1e-3, 3.0e38, 0.7071, 12345.678,
+                   2.0 ** -20, 1.0 / 2688.0], dtype=np.float32)
+
+
+def test_every_bf16_pattern_every_scale():
+    """All 65,280 finite bf16 patterns (blocks of 16 in two arrangements) under
+    ten SFScaleVal values covering both clamps, subnormal E4M3 scales and
+    reciprocal overflow: codes and scales bit-exact."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = np.isfinite(OF.bf16_to_f32(bits))
+    bits = bits[finite]
+    rng = np.random.default_rng(0)
+    arr = [bits, bits[rng.permutation(bits.size)]]
+    rows = []
+    for a in arr:
+        n = a.size // 256 * 256
+        rows.append(a[:n].reshape(-1, 256))
+    x = np.concatenate(rows)                          # [R, 256]
+    R = x.shape[0]
+    E = GS_SET.size
+    expert = np.arange(R, dtype=np.int32) % E
+    codes, sf = _gpu_quantize(x, 256, 1, expert, None, GS_SET, R)
+    oc, osf = OQ.quantize_experts(x, expert, GS_SET)
+    assert np.array_equal(sf, osf)
+    assert np.array_equal(codes, oc)
+
+
+def test_topk_scatter_and_ragged_blocks():
+    rng = np.random.default_rng(1)
+    T, K, k, E = 37, 272, 3, 5
+    x = S.f32_to_bf16_bits((rng.standard_normal((T, K)) * np.exp(rng.uniform(-4, 4, (T, 1)))).astype(np.float32))
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    gs = np.exp(rng.uniform(-3, 6, E)).astype(np.float32)
+    P = T * k
+    dst = rng.permutation(P).astype(np.int32)
+    codes, sf = _gpu_quantize(x, K, k, ids.reshape(-1), dst, gs, P)
+    src_tok = np.empty(P, dtype=np.int64)
+    src_tok[dst] = np.arange(P) // k
+    row_exp = np.empty(P, dtype=np.int64)
+    row_exp[dst] = ids.reshape(-1)
+    oc, osf = OQ.quantize_experts(x[src_tok], row_exp, gs)
+    assert np.array_equal(codes, oc) and np.array_equal(sf, osf)
+
+
+def test_null_scale_means_unit_scale():
+    rng = np.random.default_rng(2)
+    x = S.f32_to_bf16_bits(rng.standard_normal((8, 64)).astype(np.float32) * 300)
+    codes, sf = _gpu_quantize(x, 64, 1, None, None, None, 8)
+    oc, osf = OQ.quantize_experts(x, np.zeros(8, dtype=np.int64), None)
+    assert np.array_equal(codes, oc) and np.array_equal(sf, osf)
+
+
+def test_out_of_range_destinations_are_skipped():
+    rng = np.random.default_rng(3)
+    x = S.f32_to_bf16_bits(rng.standard_normal((4, 32)).astype(np.float32))
+    dst = np.array([0, 7, -1, 2], dtype=np.int32)               # 7 and -1 out of range
+    expert = np.array([0, 0, 0, 5], dtype=np.int32)             # 5 out of range
+    codes, sf = _gpu_quantize(x, 32, 1, expert, dst, np.ones(2, dtype=np.float32), 4)
+    oc, osf = OQ.quantize_experts(x[[0]], np.array([0]), np.ones(1, dtype=np.float32))
+    assert np.array_equal(codes[0], oc[0]) and np.array_equal(sf[0], osf[0])
+    assert np.all(codes[1:] == 0xAB) and np.all(sf[1:] == 0xCD)
+
+
+def test_quantizer_workload_full_size():
+    """8192 tokens x 2816, top-8 of 128 experts (uniform router), 1% outlier
+    channels x50, per-expert calibrated input scales: every code and scale
+    bit-exact, and both saturation levels are exercised."""
+    torch = _torch()
+    w = S.WORKLOADS["quant"]
+    x = S.activations(w)
+    logits = S.router_logits(w)
+    xc, lc = S.calibration_batch(w)
+    s13, wr = OM.calibrate_input_scale(xc, lc, w.k, w.E)
+    ok, gs, _ = OM.validate_scales(s13, wr)
+    assert ok
+    ids, _ = OM.route(logits, w.k)
+    offsets, src, inv = OM.permute(ids, w.E)
+    codes, sf = _gpu_quantize(x, w.H, w.k, ids.reshape(-1), inv, gs, w.P)
+    oc, osf = OQ.quantize_experts(x[src // w.k], OM.row_experts(offsets), gs)
+    assert np.array_equal(sf, osf)
+    assert np.array_equal(codes, oc)
+    assert np.count_nonzero(osf == 0x7E) > 0
+    assert np.count_nonzero((OF.unpack_nibbles(oc) & 7) == 7) > 0
+
+
+def test_zero_rows_is_noop():
+    torch = _torch()
+    from nvfp4_w4a4_expert_amd import _lib as L
+    codes = torch.full((1, 8), 7, dtype=torch.uint8, device="cuda")
+    L.quantize_experts(None, 16, 0, 16, 1, None, None, 1, None, codes, codes, 0)
+    torch.cuda.synchronize()
+    assert codes.cpu().numpy().tolist() == [[7] * 8]
