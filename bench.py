@@ -1,0 +1,341 @@
+#!/usr/bin/env python3
+"""Throughput of the NVFP4 W4A4 routed-expert MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode]
+
+A step is one ``nvfp4_moe_forward``: route -> permute -> quantise A1 ->
+grouped w13 GEMM (+SiLU*mul + requant) -> grouped w2 GEMM -> combine, on one
+batch of seeded synthetic input that is already resident in HBM.  The
+default workload is the prefill-shaped layer (4096 tokens, hidden 2816, 128
+experts, intermediate 704, top-8, biased router).  Inputs rotate over three
+sets so repeated steps are not served from the 256 MB last-level cache.
+
+Printed as one JSON line: tokens/s of the layer (``value``), the dominant
+kernel's roofline fraction (measured with HIP events on the library's
+stream), the per-stage times, the quantiser's HBM GB/s on the
+quantiser-alone workload (8192 x 2816, top-8 of 128), and the CPU oracle's
+time on a bounded sample of the same workload (``cpu_baseline``).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E peak
+MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16/bf16 MFMA peak
+
+METRIC = "NVFP4 MoE layer tokens/s (hidden 2816, 128 experts) + quantizer HBM GB/s"
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="prefill", choices=["prefill", "decode"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-quantizer", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=64)
+    return ap.parse_args()
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on its own stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def create(self, n):
+        out = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out[i] = h.value
+        return out
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, arr):
+        for h in arr:
+            self.hip.hipEventDestroy(h)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def build_layer(w, torch, M):
+    """Seeded bf16 expert weights -> NVFP4 with the library's quantiser;
+    activation scales calibrated with the library's kernels."""
+    import synthetic as S
+    t0 = time.time()
+    w13_bits, w2_bits = S.expert_weights(w)
+    w13 = M.bf16_tensor(w13_bits)
+    w2 = M.bf16_tensor(w2_bits)
+    del w13_bits, w2_bits
+    w13c, w13s, w13s2 = M.quantize_expert_weights(w13)
+    w2c, w2s, w2s2 = M.quantize_expert_weights(w2)
+    del w13, w2
+    xc, lc = S.calibration_batch(w)
+    cal = M.calibrate_layer(w13c, w13s, w13s2, w2c, w2s, w2s2, M.bf16_tensor(xc),
+                            torch.from_numpy(lc).cuda(), w.k)
+    layer = M.NVFP4MoELayer(w13c, w13s, w13s2, w2c, w2s, w2s2, cal.w13_input_scale,
+                            cal.w2_input_scale, cal.written13, cal.written2)
+    torch.cuda.synchronize()
+    log(f"layer prepared in {time.time() - t0:.1f}s")
+    return layer
+
+
+def bench_layer(args, torch, M, L, events):
+    import synthetic as S
+    w = S.WORKLOADS[args.workload]
+    layer = build_layer(w, torch, M)
+    sets = []
+    for i in range(3):
+        x = M.bf16_tensor(S.activations(w, layer=i))
+        lg = torch.from_numpy(S.router_logits(w, layer=i)).cuda()
+        sets.append((x, lg, torch.empty_like(x)))
+    wstruct = layer.weights()
+    ws = layer.workspace(w.T, w.k)
+    nbytes = ws.numel()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i, dbg=None):
+        x, lg, out = sets[i % 3]
+        L.moe_forward(wstruct, x, lg, w.T, w.k, None, out, ws, nbytes, dbg, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = events.create(2)
+    events.record(ev[0], stream)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    events.record(ev[1], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = events.elapsed_ms(ev[0], ev[1])
+    events.destroy(ev)
+    ms_step = ms_total / args.steps
+
+    # per-stage times: the same steps with events between the launches
+    nst = len(L.MOE_STAGES)
+    n2 = min(args.steps, 50)
+    evs = [events.create(nst + 1) for _ in range(n2)]
+    dbgs = [L.MoEDebug(stage_events=ctypes.cast(e, ctypes.POINTER(ctypes.c_void_p))) for e in evs]
+    for i in range(n2):
+        step(i, dbgs[i])
+    torch.cuda.synchronize()
+    stage_ms = np.zeros(nst)
+    for e in evs:
+        for s in range(nst):
+            stage_ms[s] += events.elapsed_ms(e[s], e[s + 1])
+        events.destroy(e)
+    stage_us = {name: 1000.0 * v / n2 for name, v in zip(L.MOE_STAGES, stage_ms)}
+    return w, layer, ms_step, wall, stage_us
+
+
+def bench_quantizer(args, torch, M, L, events):
+    """nvfp4_quantize_experts alone on the quantiser workload, 3 rotating
+    input/output sets (> last-level cache)."""
+    import synthetic as S
+    w = S.WORKLOADS["quant"]
+    xc, lc = S.calibration_batch(w)
+    # per-expert input scale from the calibration batch, with the library
+    dev = "cuda"
+    Tc = xc.shape[0]
+    ids = torch.empty((Tc, w.k), dtype=torch.int32, device=dev)
+    wts = torch.empty((Tc, w.k), dtype=torch.float32, device=dev)
+    off = torch.empty(w.E + 1, dtype=torch.int32, device=dev)
+    src = torch.empty(Tc * w.k, dtype=torch.int32, device=dev)
+    inv = torch.empty(Tc * w.k, dtype=torch.int32, device=dev)
+    L.route_topk(torch.from_numpy(lc).cuda(), Tc, w.E, w.k, ids, wts)
+    L.permute(ids, Tc, w.k, w.E, off, src, inv)
+    amax = torch.empty(w.E, dtype=torch.float32, device=dev)
+    L.expert_absmax(M.bf16_tensor(xc), w.H, w.H, src, w.k, off, w.E, Tc * w.k, amax)
+    s13 = (amax.cpu().numpy() / M.NVFP4_RANGE).astype(np.float32)
+    st, gs, _, _ = L.validate_scales(s13, (np.diff(off.cpu().numpy()) > 0).astype(np.uint8))
+    if st != L.OK:
+        raise RuntimeError("quantiser workload calibration left unwritten slots")
+    gs_d = torch.from_numpy(gs).cuda()
+    sets = []
+    for i in range(3):
+        x = M.bf16_tensor(S.activations(w, layer=i))
+        lg = torch.from_numpy(S.router_logits(w, layer=i)).cuda()
+        ids = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+        wts = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+        off = torch.empty(w.E + 1, dtype=torch.int32, device=dev)
+        src = torch.empty(w.P, dtype=torch.int32, device=dev)
+        inv = torch.empty(w.P, dtype=torch.int32, device=dev)
+        L.route_topk(lg, w.T, w.E, w.k, ids, wts)
+        L.permute(ids, w.T, w.k, w.E, off, src, inv)
+        codes = torch.empty((w.P, w.H // 2), dtype=torch.uint8, device=dev)
+        sf = torch.empty((w.P, w.H // 16), dtype=torch.uint8, device=dev)
+        sets.append((x, ids, inv, codes, sf))
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i):
+        x, ids, inv, codes, sf = sets[i % 3]
+        L.quantize_experts(x, w.H, w.T, w.H, w.k, ids, inv, w.E, gs_d, codes, sf, w.P, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    n = max(args.steps, 50)
+    ev = events.create(2)
+    events.record(ev[0], stream)
+    for i in range(n):
+        step(i)
+    events.record(ev[1], stream)
+    torch.cuda.synchronize()
+    us = 1000.0 * events.elapsed_ms(ev[0], ev[1]) / n
+    events.destroy(ev)
+    # algorithmic bytes: unique x once, routing ids + destinations, scales,
+    # packed codes and E4M3 block scales written
+    read = w.T * w.H * 2 + w.P * 4 * 2 + w.E * 4
+    write = w.P * (w.H // 2) + w.P * (w.H // 16)
+    gbps = (read + write) / (us * 1e-6) / 1e9
+    return dict(workload="quantizer alone: 8192 tokens x hidden 2816 bf16, top-8 of 128 experts, "
+                         "1% outlier channels x50",
+                us_per_launch=round(us, 3), algorithmic_bytes=int(read + write),
+                gbps=round(gbps, 1), peak_gbps=HBM_PEAK_GBPS, frac=round(gbps / HBM_PEAK_GBPS, 4))
+
+
+def cpu_baseline(args, w):
+    """The CPU oracle, unchanged, timed on a bounded sample of the workload:
+    its own NVFP4 layer (prepared untimed), then one layer forward over the
+    first ``cpu_sample_tokens`` tokens of the benchmark batch."""
+    import synthetic as S
+    from oracle import moe as OM
+    t0 = time.time()
+    w13, w2 = S.expert_weights(w)
+    xc, lc = S.calibration_batch(w)
+    layer = OM.prepare_layer(w13, w2, xc, lc, w.k, threads=min(16, os.cpu_count() or 1))
+    del w13, w2
+    log(f"oracle layer prepared in {time.time() - t0:.1f}s (untimed)")
+    n = args.cpu_sample_tokens
+    x = S.activations(w)[:n]
+    lg = S.router_logits(w)[:n]
+    t0 = time.perf_counter()
+    OM.layer_forward(layer, x, lg, w.k)
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    return dict(value=round(n / dt, 3), unit="tokens/s", cores=cores, kind="oracle",
+                seconds=round(dt, 2),
+                sample=f"first {n} tokens of the {args.workload} batch, one full layer forward "
+                       f"(route, permute, quantise, fp64 GEMMs over dequantised operands, "
+                       f"SiLU*mul, requant, combine); NumPy elementwise work single-threaded, "
+                       f"fp64 GEMMs on the BLAS thread pool ({cores} cores visible)")
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from nvfp4_w4a4_expert_amd import _lib as L
+    from nvfp4_w4a4_expert_amd import moe as M
+    events = HipEvents()
+
+    w, layer, ms_step, wall, stage_us = bench_layer(args, torch, M, L, events)
+    tokens_per_s = w.T / (ms_step * 1e-3)
+    log(f"layer: {ms_step * 1000:.1f} us/step, {tokens_per_s:.4g} tokens/s; stages {stage_us}")
+
+    P = w.T * w.k
+    flops_gemm1 = 2.0 * P * (2 * w.I) * w.H
+    flops_gemm2 = 2.0 * P * w.H * w.I
+    if args.workload == "prefill":
+        g1 = stage_us["gemm1_w13"]
+        ach = flops_gemm1 / (g1 * 1e-6) / 1e12
+        roofline = dict(kernel="grouped_gemm_kernel<true> (w13 + SiLU*mul + requant)",
+                        bound="mfma", achieved=round(ach, 1), peak=MFMA_F16_PEAK_TFLOPS,
+                        unit="TFLOP/s", frac=round(ach / MFMA_F16_PEAK_TFLOPS, 4), traffic=None,
+                        algorithmic_flops=flops_gemm1, us_per_launch=round(g1, 2))
+    else:
+        # weight streaming: algorithmic bytes = NVFP4 w13 of every expert hit
+        # (codes + E4M3 scales) + A1 read + A2 written
+        import synthetic as S
+        ids = np.argsort(-S.router_logits(w, layer=0), axis=1, kind="stable")[:, :w.k]
+        n_hit = int(np.unique(ids).size)
+        g1 = stage_us["gemm1_w13"]
+        nbytes = n_hit * (2 * w.I) * w.H * 9 // 16 + P * w.H * 9 // 16 + P * w.I * 9 // 16
+        ach = nbytes / (g1 * 1e-6) / 1e9
+        roofline = dict(kernel="grouped_gemm_kernel<true> (w13 + SiLU*mul + requant)",
+                        bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                        frac=round(ach / HBM_PEAK_GBPS, 4), traffic=None,
+                        algorithmic_bytes=int(nbytes), experts_hit=n_hit,
+                        us_per_launch=round(g1, 2))
+    gemm_us = stage_us["gemm1_w13"] + stage_us["gemm2_w2"]
+    gemms = dict(us=round(gemm_us, 2),
+                 tflops=round((flops_gemm1 + flops_gemm2) / (gemm_us * 1e-6) / 1e12, 1),
+                 frac_of_f16_peak=round((flops_gemm1 + flops_gemm2) / (gemm_us * 1e-6) / 1e12
+                                        / MFMA_F16_PEAK_TFLOPS, 4))
+
+    quant = None
+    if not args.no_quantizer:
+        quant = bench_quantizer(args, torch, M, L, events)
+        log(f"quantizer: {quant}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, w)
+        log(f"cpu baseline: {cpu}")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{args.workload} MoE layer: {w.T} tokens, hidden {w.H}, {w.E} experts, "
+                         f"intermediate {w.I}, top-{w.k}, NVFP4 W4A4 (E2M1 + E4M3/16 + fp32), "
+                         f"fp16 MFMA over exactly dequantised operands, fp32 accumulate"),
+            "tokens": w.T, "hidden": w.H, "experts": w.E, "inter": w.I, "topk": w.k,
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "expert_gemms": gemms,
+        "quantizer": quant,
+        "host_wall_s": round(wall, 4),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -13,8 +13,9 @@ pytestmark = pytest.mark.gpu
 
 
 def _report(label, m):
-    print(f"[{label}] C1 max {m['c1_max']:.2e}  h max {m['h_max']:.2e}  C2 max {m['c2_max']:.2e}  "
-          f"out max {m['out_max']:.2e} (median {m['out_median']:.2e})  e2e max {m['e2e_max']:.2e}  "
+    print(f"[{label}] rel-L2 per row: C1 max {m['c1_max']:.2e}  h max {m['h_max']:.2e}  "
+          f"C2 max {m['c2_max']:.2e}  out max {m['out_max']:.2e} (median {m['out_median']:.2e}; "
+          f"vs bf16(ref) {m['out_vs_rounded_max']:.2e})  e2e max {m['e2e_max']:.2e}  "
           f"A2 bytes differing from oracle-own A2 {m['a2_byte_diffs_vs_own']}", flush=True)
 
 
@@ -109,34 +110,3 @@ def test_stack_layer(layer_idx):
     m = check_layer_parity(layer, x, logits, w.k, residual_bits=x, label=f"stack L{layer_idx}")
     assert np.count_nonzero(np.diff(m["ref"]["offsets"]) == 0) >= 1
     _report(f"stack L{layer_idx}", m)
-
-
-def test_stack_bad_scales_rejected_at_load():
-    """The 30-layer stack's scale-validation case: three seeded corrupt slots
-    (NaN, unwritten with a valid-looking stale value, unwritten with -inf
-    bits) are named exactly and nothing is uploaded."""
-    from nvfp4_w4a4_expert_amd import moe as M
-    w = S.WORKLOADS["stack"]
-    s13 = np.full(w.E, 1.0 / 2688, dtype=np.float32)
-    s2 = np.full(w.E, 1.0 / 2688, dtype=np.float32)
-    wr13 = np.ones(w.E, dtype=np.uint8)
-    wr2 = np.ones(w.E, dtype=np.uint8)
-    for proj, e, kind in S.bad_scale_slots(w):
-        s, wr = (s13, wr13) if proj == "w13" else (s2, wr2)
-        if kind == "nan":
-            s[e] = np.nan
-        elif kind == "unwritten_garbage":
-            s[e] = np.float32(0.25)
-            wr[e] = 0
-        else:
-            s[e] = -np.inf
-            wr[e] = 0
-    bad13 = sorted(e for p, e, _ in S.bad_scale_slots(w) if p == "w13")
-    bad2 = sorted(e for p, e, _ in S.bad_scale_slots(w) if p == "w2")
-    with pytest.raises(M.BadScaleError) as ei:
-        M.NVFP4MoELayer(None, None, None, None, None, None, s13, s2, wr13, wr2, device="cuda")
-    assert ei.value.projection == "w13" and ei.value.bad_slots == bad13
-    s13_ok = np.full(w.E, 1.0 / 2688, dtype=np.float32)
-    with pytest.raises(M.BadScaleError) as ei:
-        M.NVFP4MoELayer(None, None, None, None, None, None, s13_ok, s2, None, wr2, device="cuda")
-    assert ei.value.projection == "w2" and ei.value.bad_slots == bad2
