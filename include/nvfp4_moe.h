@@ -192,6 +192,20 @@ NVFP4_API nvfp4_status_t nvfp4_expert_absmax(const void* x_bf16, int64_t ldx, in
                                              nvfp4_stream_t stream);
 
 /*
+ * nvfp4_selftest_conversions — device self-check of the three gfx950
+ * conversion instructions the kernels use, each against a reference built
+ * from the format definitions (page 3, "NVFP4" section: the E2M1 code table;
+ * encoding rounds to nearest with ties to even and saturates to 6; E4M3 block
+ * scales).  mismatches: device uint64[3], written asynchronously:
+ *   [0] fp32 -> E2M1 encode vs midpoint comparisons, every non-NaN fp32 input;
+ *   [1] E2M1 byte -> fp16 pair vs the code table, all 256 bytes x 4 positions;
+ *   [2] E4M3 -> fp16 vs the OCP E4M3 definition, all 254 non-NaN codes.
+ * All three must read 0.
+ */
+NVFP4_API nvfp4_status_t nvfp4_selftest_conversions(unsigned long long* mismatches,
+                                                    nvfp4_stream_t stream);
+
+/*
  * One MoE layer's NVFP4 expert weights and scales — the checkpoint fields of
  * page 3 ("ROOT CAUSE" and the glossary's static weight quantisation entry:
  * w13/w2 packed FP4 weights, weight_scale (E4M3 per 16), weight_scale_2

@@ -61,6 +61,7 @@ _SIGS = {
     "nvfp4_route_topk": (_i32, [_p, _i32, _i32, _i32, _p, _p, _p]),
     "nvfp4_permute": (_i32, [_p, _i32, _i32, _i32, _p, _p, _p, _p]),
     "nvfp4_expert_absmax": (_i32, [_p, _i64, _i32, _p, _i32, _p, _i32, _i32, _p, _p]),
+    "nvfp4_selftest_conversions": (_i32, [_p, _p]),
     "nvfp4_moe_workspace_size": (_i32, [_i32, _i32, ctypes.POINTER(MoEWeights), ctypes.POINTER(ctypes.c_size_t)]),
     "nvfp4_moe_forward": (_i32, [ctypes.POINTER(MoEWeights), _p, _p, _i32, _i32, _p, _p, _p,
                                  ctypes.c_size_t, ctypes.POINTER(MoEDebug), _p]),
@@ -146,6 +147,11 @@ def expert_absmax(x, ldx: int, K: int, src, src_div: int, expert_offsets, num_ex
     _check(_lib.nvfp4_expert_absmax(_ptr(x), ldx, K, _ptr(src), src_div, _ptr(expert_offsets),
                                     num_experts, num_rows, _ptr(amax_out), _stream(stream)),
            "nvfp4_expert_absmax")
+
+
+def selftest_conversions(mismatches, stream=None):
+    _check(_lib.nvfp4_selftest_conversions(_ptr(mismatches), _stream(stream)),
+           "nvfp4_selftest_conversions")
 
 
 def moe_workspace_size(num_tokens: int, k: int, weights: MoEWeights) -> int:

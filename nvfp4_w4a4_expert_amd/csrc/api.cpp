@@ -164,6 +164,12 @@ NVFP4_API nvfp4_status_t nvfp4_expert_absmax(const void* x_bf16, int64_t ldx, in
                                      static_cast<hipStream_t>(stream)));
 }
 
+NVFP4_API nvfp4_status_t nvfp4_selftest_conversions(unsigned long long* mismatches,
+                                                    nvfp4_stream_t stream) {
+  if (!mismatches) return NVFP4_ERR_INVALID_ARG;
+  return device_status(launch_conversions_selftest(mismatches, static_cast<hipStream_t>(stream)));
+}
+
 NVFP4_API nvfp4_status_t nvfp4_moe_workspace_size(int32_t num_tokens, int32_t k,
                                                   const nvfp4_moe_weights_t* w, size_t* bytes) {
   if (!bytes || !w || num_tokens < 0 || k < 1) return NVFP4_ERR_INVALID_ARG;

@@ -14,22 +14,38 @@
 // The contraction runs on v_mfma_f32_32x32x16_f16 with fp32 accumulation;
 // alpha is applied once in the fp32 epilogue.
 //
-// Tiling: 256 threads (4 wavefronts, 2 x 2), a 128 x 128 output tile, K in
-// steps of 64.  Each step, every thread loads 16 bytes of packed codes and
-// 2 scale bytes of one A row and one B row, converts them to 32 fp16 values
-// with the gfx950 FP4 -> fp16 conversion plus one packed fp16 multiply by
-// the block scale, and stores them to LDS (double-buffered, rows padded by
-// 16 bytes).  Each wavefront then issues 16 MFMAs on a 64 x 64 sub-tile.
-// The K order inside a step is permuted identically for A and B so that each
-// lane's MFMA operand is 16 contiguous LDS bytes; the sum is unchanged.
+// Work split.  A workgroup owns BM token rows of one expert (BM = 32 * kMB)
+// and 64 * kWaves weight rows; wavefront w owns weight rows [64w, 64w + 64)
+// of the tile and all BM token rows.
+//  * The token operand A is shared by every wavefront: each K step it is
+//    loaded once per workgroup, dequantised to fp16 and staged in LDS
+//    (double buffered, rows padded by 16 bytes so the 16-byte fragment reads
+//    of 16 consecutive lanes hit distinct banks).
+//  * The weight operand B is private to its wavefront: each lane streams its
+//    row's packed codes straight from global memory into registers two K
+//    steps ahead and dequantises 8 values per MFMA just before use (the
+//    gfx950 FP4 -> fp16 pair conversion, then one packed fp16 multiply by the
+//    block scale).  Weights never pass through LDS.
+//  * K order inside a step is permuted identically for A and B so that each
+//    lane's operand is contiguous: lane group g = lane / 32 covers k in
+//    [g * BK/2, (g + 1) * BK/2) of a BK-wide step, 8 values per MFMA
+//    (BK = 128 for w13, 64 for w2 whose K = I need not be a multiple of 128).
 //
-// Grouping: a tile is (expert e, m-tile of e's rows, n-tile).  The m-tiles of
-// all experts are numbered consecutively; every workgroup recomputes the
-// per-expert tile prefix from expert_offsets (E <= 1024) and finds its
-// expert, so no host synchronisation is needed and experts with no rows cost
-// nothing.  Rows past an expert's last row read a valid row and are not
-// stored.  For GEMM1 an n-tile holds 64 gate columns and the matching 64 up
-// columns, so SiLU*mul happens in registers.
+// Grouping and scheduling.  A tile is (expert, m-tile of the expert's rows,
+// n-tile).  m-tiles of all experts are numbered consecutively; each
+// workgroup recomputes the per-expert tile prefix from expert_offsets
+// (E <= 1024) and finds its expert, so no host synchronisation is needed and
+// experts without rows cost nothing.  The 1-D grid is remapped so that the
+// workgroups the hardware sends to one XCD (round robin over 8) get a
+// contiguous range of tiles: all n-tiles of an m-tile, and consecutive
+// m-tiles of the same expert, share that XCD's L2.  Rows past an expert's
+// last row read a valid row and are not stored.
+//
+// GEMM1 pairs columns: wavefront w's 64 weight rows are 32 gate rows and the
+// 32 matching up rows, so SiLU*mul happens in registers and the tile's h
+// columns are requantised from LDS in blocks of 16.
+#include <type_traits>
+
 #include "internal.h"
 #include "nvfp4_device.h"
 
@@ -40,40 +56,45 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 64, kThreads = 256;
-constexpr int kLd = kBK + 8;                         // fp16 per LDS row (16-byte pad)
-constexpr int kStageHalves = (kBM + kBN) * kLd;      // A rows then B rows
-constexpr int kLdsBytes = 2 * kStageHalves * 2;      // double buffered: 73728 B
+constexpr int kXcds = 8;
 
-// 32 consecutive E2M1 codes (16 bytes) with the E4M3 scales of their two
-// 16-element blocks -> 32 exact fp16 values (16 half2, element order kept).
-__device__ __forceinline__ void dequant32(const uint4 c, uint32_t sf2, half2_t* out) {
-  const _Float16 s0 = (_Float16)e4m3_decode(sf2 & 0xFFu);
-  const _Float16 s1 = (_Float16)e4m3_decode((sf2 >> 8) & 0xFFu);
-  const half2_t h0 = {s0, s0}, h1 = {s1, s1};
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    out[4 * i + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 0) * (i < 2 ? h0 : h1);
-    out[4 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 1) * (i < 2 ? h0 : h1);
-    out[4 * i + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 2) * (i < 2 ? h0 : h1);
-    out[4 * i + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 3) * (i < 2 ? h0 : h1);
-  }
+template <int V>
+using Int = std::integral_constant<int, V>;
+
+// 8 E2M1 codes (one 32-bit word) -> 8 exact fp16 values scaled by `s`.
+__device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t s) {
+  const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+  const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+  const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+  const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+  return half8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
-// Block-wide search of the grouped m-tile `mt`: returns false when mt is past
-// the last tile.  s_scan needs 6 ints of LDS.
+// Two E4M3 block scales (the low 16 bits of `w`, or the high 16 bits when
+// kHi) -> their exact fp16 values, with the gfx950 FP8 -> fp16 conversion.
+template <bool kHi>
+__device__ __forceinline__ half2_t scales_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHi);
+}
+
+__device__ __forceinline__ half2_t bcast_lo(half2_t v) { return half2_t{v.x, v.x}; }
+__device__ __forceinline__ half2_t bcast_hi(half2_t v) { return half2_t{v.y, v.y}; }
+
+// Block-wide search of grouped m-tile `mt` (tiles of `bm` rows): false when
+// mt is past the last tile.  s_scan: 8 ints of LDS.  Threads own experts in
+// chunks of 4 * (1024 / blockDim) so any E <= 1024 is covered.
+template <int kThreads>
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int32_t E,
-                                          int32_t mt, int32_t* s_scan, int32_t& e_out,
-                                          int32_t& row0, int32_t& rows) {
+                                          int32_t mt, int32_t bm, int32_t* s_scan,
+                                          int32_t& e_out, int32_t& row0, int32_t& rows) {
+  constexpr int kPer = 1024 / kThreads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // thread tid owns experts [4 tid, 4 tid + 4)
-  int32_t cnt[4], m[4], total = 0;
+  int32_t cnt[kPer], total = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int32_t e = 4 * tid + i;
-    m[i] = e < E ? offsets[e + 1] - offsets[e] : 0;
-    cnt[i] = (m[i] + kBM - 1) / kBM;
+  for (int i = 0; i < kPer; ++i) {
+    const int32_t e = kPer * tid + i;
+    const int32_t m = e < E ? offsets[e + 1] - offsets[e] : 0;
+    cnt[i] = (m + bm - 1) / bm;
     total += cnt[i];
   }
   int32_t incl = total;
@@ -83,176 +104,302 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
     if (lane >= off) incl += o;
   }
   if (lane == 63) s_scan[wave] = incl;
-  if (tid == 0) s_scan[4] = -1;
+  if (tid == 0) s_scan[6] = -1;
   __syncthreads();
   int32_t base = incl - total;
   for (int w = 0; w < wave; ++w) base += s_scan[w];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kPer; ++i) {
     if (mt >= base && mt < base + cnt[i]) {
-      s_scan[4] = 4 * tid + i;
-      s_scan[5] = mt - base;
+      s_scan[6] = kPer * tid + i;
+      s_scan[7] = mt - base;
     }
     base += cnt[i];
   }
   __syncthreads();
-  if (s_scan[4] < 0) return false;
-  e_out = s_scan[4];
-  const int32_t local = s_scan[5];
-  row0 = offsets[e_out] + local * kBM;
-  rows = min(kBM, offsets[e_out + 1] - row0);
+  if (s_scan[6] < 0) return false;
+  e_out = s_scan[6];
+  row0 = offsets[e_out] + s_scan[7] * bm;
+  rows = min(bm, offsets[e_out + 1] - row0);
   return true;
 }
 
+struct GemmParams {
+  const uint8_t* a_codes;   // [P, K/2]
+  const uint8_t* a_sf;      // [P, K/16]
+  const uint8_t* w_codes;   // [E, N_w, K/2]
+  const uint8_t* w_sf;      // [E, N_w, K/16]
+  const float* in_scale;    // [E]
+  const float* w_scale2;    // [E]
+  const int32_t* offsets;   // [E+1]
+  int32_t E, K, N_w, I;     // N_w: weight rows per expert; I: GEMM1 h width
+  int32_t n_tiles, m_tiles_bound, grid_per_xcd;
+  // GEMM2 output
+  float* c_out;             // [P, ldc]
+  int32_t ldc;
+  // GEMM1 epilogue
+  const float* out_gscale;  // [E]
+  uint8_t* out_codes;       // [P, I/2]
+  uint8_t* out_sf;          // [P, I/16]
+  float* c1_dbg;            // [P, 2I] or null
+  uint16_t* h_dbg;          // [P, I] or null
+};
+
 }  // namespace
 
-template <bool kGated>
-__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
-    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_sf,
-    const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_sf,
-    const float* __restrict__ in_scale, const float* __restrict__ w_scale2,
-    const int32_t* __restrict__ offsets, int32_t E, int32_t K, int32_t N_w, int32_t I,
-    // GEMM2 output
-    float* __restrict__ c_out, int32_t ldc,
-    // GEMM1 epilogue
-    const float* __restrict__ out_gscale, uint8_t* __restrict__ out_codes,
-    uint8_t* __restrict__ out_sf, float* __restrict__ c1_dbg, uint16_t* __restrict__ h_dbg) {
-  extern __shared__ __align__(16) _Float16 smem[];
+template <int kWaves, int kMB, int kBK, bool kGated>
+__global__ __launch_bounds__(64 * kWaves) void grouped_gemm_kernel(const GemmParams prm) {
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kBM = 32 * kMB;
+  constexpr int kLdA = kBK + 8;                          // fp16 per LDS row (16-byte pad)
+  constexpr int kChunks = kBM * (kBK / 32);              // 32-element A chunks per step
+  constexpr int kChunksPerThread = (kChunks + kThreads - 1) / kThreads;
+  constexpr int kVec = kBK / 64;                         // 16-byte B loads per block per step
+  constexpr int kSteps = kBK / 16;                       // MFMAs (per block pair) per step
+  __shared__ __align__(16) _Float16 smem[2 * kBM * kLdA];
   __shared__ int32_t s_scan[8];
 
+  // XCD-aware remap of the hardware workgroup id to a logical tile id
+  const int32_t hw = blockIdx.x;
+  const int32_t logical = (hw % kXcds) * prm.grid_per_xcd + hw / kXcds;
+  const int32_t mt = logical / prm.n_tiles;
+  const int32_t nt = logical - mt * prm.n_tiles;
+  if (mt >= prm.m_tiles_bound) return;
   int32_t e, row0, rows;
-  if (!find_tile(offsets, E, (int32_t)blockIdx.y, s_scan, e, row0, rows)) return;
+  if (!find_tile<kThreads>(prm.offsets, prm.E, mt, kBM, s_scan, e, row0, rows)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int32_t nt = blockIdx.x;
-  // n0: first output column of the tile (gate column for GEMM1)
-  const int32_t n0 = kGated ? nt * 64 : nt * kBN;
-
-  // this thread's load assignment: row r (0..127) of A and of B, K half hk
-  const int r = tid >> 1, hk = tid & 1;
+  const int32_t K = prm.K;
   const int64_t kb2 = K / 2, kb16 = K / 16;
-  const int32_t a_row = row0 + min(r, rows - 1);
-  const uint8_t* a_cp = a_codes + (int64_t)a_row * kb2 + 16 * hk;
-  const uint8_t* a_sp = a_sf + (int64_t)a_row * kb16 + 2 * hk;
-  int32_t w_row;
-  if (kGated) w_row = r < 64 ? n0 + r : I + n0 + (r - 64);
-  else w_row = n0 + r;
-  const int64_t w_base = (int64_t)e * N_w + w_row;
-  const uint8_t* b_cp = w_codes + w_base * kb2 + 16 * hk;
-  const uint8_t* b_sp = w_sf + w_base * kb16 + 2 * hk;
+  const int nk = K / kBK;
 
-  f32x16_t acc[2][2];
+  // ---- A staging assignment: chunk c -> (row, 32-wide k chunk) --------------
+  const uint8_t* a_cp[kChunksPerThread];
+  const uint8_t* a_sp[kChunksPerThread];
+  int a_lds[kChunksPerThread];
+  bool a_on[kChunksPerThread];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kChunksPerThread; ++i) {
+    const int c = tid + i * kThreads;
+    a_on[i] = c < kChunks;
+    const int cc = a_on[i] ? c : 0;
+    const int r = cc / (kBK / 32), kc = cc % (kBK / 32);
+    const int64_t arow = row0 + min(r, rows - 1);
+    a_cp[i] = prm.a_codes + arow * kb2 + 16 * kc;
+    a_sp[i] = prm.a_sf + arow * kb16 + 2 * kc;
+    a_lds[i] = r * kLdA + 32 * kc;
+  }
+
+  // ---- B streaming assignment: wave's 64 weight rows, 2 blocks of 32 ------
+  // GEMM1: block 0 = gate rows, block 1 = the matching up rows.
+  const int32_t hc0 = kGated ? nt * (32 * kWaves) + 32 * wave : 0;   // h column base
+  const int32_t n0 = kGated ? 0 : nt * (64 * kWaves) + 64 * wave;    // output column base
+  const bool active = kGated ? hc0 < prm.I : n0 < prm.N_w;
+  const int g = lane >> 5;
+  const uint8_t* b_cp[2];
+  const uint8_t* b_sp[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    int32_t wrow;
+    if (kGated) wrow = (j == 0 ? hc0 : prm.I + hc0) + (lane & 31);
+    else wrow = n0 + 32 * j + (lane & 31);
+    if (!active) wrow = 0;
+    const int64_t base = (int64_t)e * prm.N_w + wrow;
+    b_cp[j] = prm.w_codes + base * kb2 + (kBK / 4) * g;
+    b_sp[j] = prm.w_sf + base * kb16 + (kBK / 32) * g;
+  }
+
+  f32x16_t acc[kMB][2];
+#pragma unroll
+  for (int i = 0; i < kMB; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
 
-  const int nk = K / kBK;
-  uint4 ac = *reinterpret_cast<const uint4*>(a_cp);
-  uint32_t as = *reinterpret_cast<const uint16_t*>(a_sp);
-  uint4 bc = *reinterpret_cast<const uint4*>(b_cp);
-  uint32_t bs = *reinterpret_cast<const uint16_t*>(b_sp);
+  u32x4 a_raw[kChunksPerThread];
+  uint32_t a_sraw[kChunksPerThread];
+  u32x4 b_raw[2][2][kVec];    // [buffer][block][16-byte piece]
+  uint32_t b_sraw[2][2];      // [buffer][block]: kBK/32 scale bytes
 
-  auto stage_store = [&](int st) {
-    half2_t v[16];
-    _Float16* base = smem + st * kStageHalves;
-    dequant32(ac, as, v);
-    uint4* dst = reinterpret_cast<uint4*>(base + r * kLd + 32 * hk);
+  auto load_a = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = *reinterpret_cast<const uint4*>(&v[4 * i]);
-    dequant32(bc, bs, v);
-    dst = reinterpret_cast<uint4*>(base + (kBM + r) * kLd + 32 * hk);
+    for (int i = 0; i < kChunksPerThread; ++i) {
+      if (!a_on[i]) continue;
+      a_raw[i] = *reinterpret_cast<const u32x4*>(a_cp[i] + (int64_t)kt * (kBK / 2));
+      a_sraw[i] = *reinterpret_cast<const uint16_t*>(a_sp[i] + (int64_t)kt * (kBK / 16));
+    }
+  };
+  auto store_a = [&](auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    _Float16* base = smem + buf * (kBM * kLdA);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = *reinterpret_cast<const uint4*>(&v[4 * i]);
+    for (int i = 0; i < kChunksPerThread; ++i) {
+      if (!a_on[i]) continue;
+      const half2_t sp = scales_f16<false>(a_sraw[i]);
+      const half2_t s0 = bcast_lo(sp), s1 = bcast_hi(sp);
+      half8_t* dst = reinterpret_cast<half8_t*>(base + a_lds[i]);
+      dst[0] = dequant8(a_raw[i].x, s0);
+      dst[1] = dequant8(a_raw[i].y, s0);
+      dst[2] = dequant8(a_raw[i].z, s1);
+      dst[3] = dequant8(a_raw[i].w, s1);
+    }
+  };
+  auto load_b = [&](int kt, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(b_cp[j] + (int64_t)kt * (kBK / 2));
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) b_raw[buf][j][v] = src[v];
+      const uint8_t* sp = b_sp[j] + (int64_t)kt * (kBK / 16);
+      if constexpr (kBK == 128) b_sraw[buf][j] = *reinterpret_cast<const uint32_t*>(sp);
+      else b_sraw[buf][j] = *reinterpret_cast<const uint16_t*>(sp);
+    }
+  };
+  // One K step: kSteps MFMA rounds of (kMB x 2) 32x32x16 products.  The
+  // operands of round s+1 (B dequantised from registers, A read from LDS) are
+  // produced while round s's MFMAs run; the scheduling groups below interleave
+  // one MFMA with the next round's conversions and LDS reads so the matrix
+  // core is fed from a single wavefront.
+  auto compute = [&](auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const _Float16* abase = smem + buf * (kBM * kLdA) + (lane & 31) * kLdA + (kBK / 2) * g;
+    // block scales of this step: kBK/32 per block, as fp16 pairs
+    half2_t sc[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      sc[j][0] = scales_f16<false>(b_sraw[buf][j]);
+      sc[j][1] = kBK == 128 ? scales_f16<true>(b_sraw[buf][j]) : sc[j][0];
+    }
+    auto bdeq = [&](int st, int j) -> half8_t {
+      const u32x4& v = b_raw[buf][j][st >> 2];
+      const uint32_t word = (st & 3) == 0 ? v.x : (st & 3) == 1 ? v.y : (st & 3) == 2 ? v.z : v.w;
+      const half2_t pair = sc[j][(st >> 2) & 1];
+      return dequant8(word, ((st >> 1) & 1) ? bcast_hi(pair) : bcast_lo(pair));
+    };
+    auto aread = [&](int st, int i) -> half8_t {
+      return *reinterpret_cast<const half8_t*>(abase + i * 32 * kLdA + 8 * st);
+    };
+    half8_t bf[2], af[kMB];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) bf[j] = bdeq(0, j);
+#pragma unroll
+    for (int i = 0; i < kMB; ++i) af[i] = aread(0, i);
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      half8_t nbf[2], naf[kMB];
+      if (st + 1 < kSteps) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) nbf[j] = bdeq(st + 1, j);
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) naf[i] = aread(st + 1, i);
+      }
+#pragma unroll
+      for (int i = 0; i < kMB; ++i) {
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[0], acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[1], acc[i][1], 0, 0, 0);
+      }
+      if (st + 1 < kSteps) {
+#pragma unroll
+        for (int m = 0; m < 2 * kMB; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 8 / kMB, 0); // next round's conversions
+          if (m < kMB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bf[j] = nbf[j];
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) af[i] = naf[i];
+      }
+    }
   };
 
-  stage_store(0);
-  __syncthreads();
-
-  // A sub-tile rows of this wave, B sub-tile rows (in the LDS B block)
-  const int a_r0 = wm * 64 + (lane & 31);
-  const int b_r0 = kGated ? wn * 32 + (lane & 31) : wn * 64 + (lane & 31);
-  const int b_r1 = kGated ? 64 + wn * 32 + (lane & 31) : wn * 64 + 32 + (lane & 31);
-  const int kg = 32 * (lane >> 5);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) {
-      const int64_t koff2 = (int64_t)(kt + 1) * (kBK / 2), koff16 = (kt + 1) * (kBK / 16);
-      ac = *reinterpret_cast<const uint4*>(a_cp + koff2);
-      as = *reinterpret_cast<const uint16_t*>(a_sp + koff16);
-      bc = *reinterpret_cast<const uint4*>(b_cp + koff2);
-      bs = *reinterpret_cast<const uint16_t*>(b_sp + koff16);
-    }
-    const _Float16* base = smem + st * kStageHalves;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int kk = kg + 8 * s;
-      const half8_t a0 = *reinterpret_cast<const half8_t*>(base + a_r0 * kLd + kk);
-      const half8_t a1 = *reinterpret_cast<const half8_t*>(base + (a_r0 + 32) * kLd + kk);
-      const half8_t b0 = *reinterpret_cast<const half8_t*>(base + (kBM + b_r0) * kLd + kk);
-      const half8_t b1 = *reinterpret_cast<const half8_t*>(base + (kBM + b_r1) * kLd + kk);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, acc[1][1], 0, 0, 0);
-    }
-    if (kt + 1 < nk) stage_store(st ^ 1);
-    __syncthreads();
+  // ---- pipeline: step kt runs the MFMAs on buffer kt&1 while A(kt+1) is
+  // dequantised into the other LDS buffer and A(kt+2), B(kt+2) are in flight.
+  // Full pairs of steps run in a loop with no early exit (so the accumulators
+  // stay in place); an odd last step follows it.
+  load_a(0);
+  load_b(0, Int<0>{});
+  store_a(Int<0>{});
+  if (nk > 1) {
+    load_a(1);
+    load_b(1, Int<1>{});
   }
+  __syncthreads();
+  auto step = [&](int kt, auto rc) {
+    constexpr int r = decltype(rc)::value;
+    compute(Int<r>{});
+    if (kt + 1 < nk) store_a(Int<r ^ 1>{});
+    if (kt + 2 < nk) {
+      load_a(kt + 2);
+      load_b(kt + 2, Int<r>{});
+    }
+    __syncthreads();
+  };
+  const int nk2 = nk & ~1;
+  for (int kt = 0; kt < nk2; kt += 2) {
+    step(kt, Int<0>{});
+    step(kt + 1, Int<1>{});
+  }
+  if (nk2 < nk) step(nk2, Int<0>{});
 
-  const float alpha = in_scale[e] * w_scale2[e];
+  const float alpha = prm.in_scale[e] * prm.w_scale2[e];
   // MFMA 32x32 output layout: lane holds column (lane & 31) and rows
   // 8 * (i / 4) + 4 * (lane / 32) + (i % 4) for accumulator element i.
-  const int ccol = lane & 31, crow = 4 * (lane >> 5);
+  const int ccol = lane & 31, crow = 4 * g;
 
   if constexpr (!kGated) {
+    if (!active) return;
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < kMB; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int row = wm * 64 + mi * 32 + 8 * (i >> 2) + crow + (i & 3);
-          const int col = n0 + wn * 64 + ni * 32 + ccol;
-          if (row < rows) c_out[(int64_t)(row0 + row) * ldc + col] = alpha * acc[mi][ni][i];
+          const int row = mi * 32 + 8 * (i >> 2) + crow + (i & 3);
+          if (row < rows)
+            prm.c_out[(int64_t)(row0 + row) * prm.ldc + n0 + 32 * j + ccol] = alpha * acc[mi][j][i];
         }
   } else {
-    // SiLU(gate) * up -> bf16 tile [128][64] in LDS (reusing the stage buffers;
-    // the loop's last barrier ordered every wave's final LDS reads before this)
+    // SiLU(gate) * up -> bf16 tile [BM][32 * kWaves] in LDS (the stage buffers
+    // are free: the loop's last barrier ordered all reads of them)
+    constexpr int kHW = 32 * kWaves;
+    constexpr int kLdh = kHW + 8;
+    static_assert(kLdh <= 2 * kLdA, "h tile must fit the stage buffers");
     uint16_t* sh = reinterpret_cast<uint16_t*>(smem);
-    constexpr int kLdh = 64 + 8;
+    const int32_t hbase = nt * kHW;
+    const int32_t I = prm.I;
+    if (active) {
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < kMB; ++mi)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = wm * 64 + mi * 32 + 8 * (i >> 2) + crow + (i & 3);
-        const int col = wn * 32 + ccol;
-        const float g = alpha * acc[mi][0][i];
-        const float u = alpha * acc[mi][1][i];
-        const float hv = g / (1.0f + __expf(-g)) * u;
-        const uint32_t hb = f32_to_bf16(hv);
-        sh[row * kLdh + col] = (uint16_t)hb;
-        if (row < rows) {
-          const int64_t p = row0 + row;
-          if (c1_dbg) {
-            c1_dbg[p * 2 * I + n0 + col] = g;
-            c1_dbg[p * 2 * I + I + n0 + col] = u;
+        for (int i = 0; i < 16; ++i) {
+          const int row = mi * 32 + 8 * (i >> 2) + crow + (i & 3);
+          const int col = 32 * wave + ccol;
+          const float gv = alpha * acc[mi][0][i];
+          const float uv = alpha * acc[mi][1][i];
+          const float hv = gv / (1.0f + __expf(-gv)) * uv;
+          const uint32_t hb = f32_to_bf16(hv);
+          sh[row * kLdh + col] = (uint16_t)hb;
+          if (row < rows) {
+            const int64_t p = row0 + row;
+            if (prm.c1_dbg) {
+              prm.c1_dbg[p * 2 * I + hbase + col] = gv;
+              prm.c1_dbg[p * 2 * I + I + hbase + col] = uv;
+            }
+            if (prm.h_dbg) prm.h_dbg[p * I + hbase + col] = (uint16_t)hb;
           }
-          if (h_dbg) h_dbg[p * I + n0 + col] = (uint16_t)hb;
         }
-      }
+    }
     __syncthreads();
-    // requantise: 128 rows x 4 blocks of 16 columns; two blocks per thread
-    const float gs = out_gscale[e];
+    // requantise: BM rows x (kHW / 16) blocks of 16 columns
+    constexpr int kItems = kBM * (kHW / 16);
+    const float gs = prm.out_gscale[e];
     const int64_t ob2 = I / 2, ob16 = I / 16;
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int item = tid + kThreads * it;
-      const int row = item >> 2, blk = item & 3;
-      if (row < rows) {
-        const uint4* src = reinterpret_cast<const uint4*>(sh + row * kLdh + 16 * blk);
+    for (int item = tid; item < kItems; item += kThreads) {
+      const int row = item / (kHW / 16), blk = item % (kHW / 16);
+      const int32_t hcol = hbase + 16 * blk;
+      if (row < rows && hcol < I) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(sh + row * kLdh + 16 * blk);
         float xv[16];
         unpack_bf16x8(src[0], xv);
         unpack_bf16x8(src[1], xv + 8);
@@ -261,49 +408,60 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
         wv.x = encode8(xv, bsc.inv);
         wv.y = encode8(xv + 8, bsc.inv);
         const int64_t p = row0 + row;
-        *reinterpret_cast<uint2*>(out_codes + p * ob2 + (n0 + 16 * blk) / 2) = wv;
-        out_sf[p * ob16 + n0 / 16 + blk] = (uint8_t)bsc.sf;
+        *reinterpret_cast<uint2*>(prm.out_codes + p * ob2 + hcol / 2) = wv;
+        prm.out_sf[p * ob16 + hcol / 16] = (uint8_t)bsc.sf;
       }
     }
   }
 }
 
-static int32_t m_tiles_bound(int32_t P, int32_t E) {
-  return (P + kBM - 1) / kBM + (P < E ? P : E);
+namespace {
+
+int32_t m_tiles_bound(int32_t P, int32_t E, int32_t bm) {
+  return (P + bm - 1) / bm + (P < E ? P : E);
 }
 
+template <int kWaves, int kMB, int kBK, bool kGated>
+hipError_t launch(GemmParams prm, int32_t P, hipStream_t stream) {
+  constexpr int kBM = 32 * kMB;
+  prm.m_tiles_bound = m_tiles_bound(P, prm.E, kBM);
+  const int64_t tiles = (int64_t)prm.m_tiles_bound * prm.n_tiles;
+  prm.grid_per_xcd = (int32_t)((tiles + kXcds - 1) / kXcds);
+  const int64_t grid = (int64_t)prm.grid_per_xcd * kXcds;
+  hipLaunchKernelGGL((grouped_gemm_kernel<kWaves, kMB, kBK, kGated>), dim3((uint32_t)grid),
+                     dim3(64 * kWaves), 0, stream, prm);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Tile height: 64 token rows when experts average at least 32 rows (prefill),
+// else 32 (decode-like batches, weight-streaming bound).
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream) {
   if (a.P == 0) return hipSuccess;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_kernel<true>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
-  const dim3 grid(a.I / 64, m_tiles_bound(a.P, a.E));
-  hipLaunchKernelGGL(grouped_gemm_kernel<true>, grid, dim3(kThreads), kLdsBytes, stream, a.a_codes,
-                     a.a_sf, a.w_codes, a.w_sf, a.in_scale, a.w_scale2, a.offsets, a.E, a.H,
-                     2 * a.I, a.I, (float*)nullptr, 0, a.out_gscale, a.out_codes, a.out_sf,
-                     a.c1_dbg, a.h_dbg);
-  return hipGetLastError();
+  GemmParams prm{};
+  prm.a_codes = a.a_codes; prm.a_sf = a.a_sf; prm.w_codes = a.w_codes; prm.w_sf = a.w_sf;
+  prm.in_scale = a.in_scale; prm.w_scale2 = a.w_scale2; prm.offsets = a.offsets;
+  prm.E = a.E; prm.K = a.H; prm.N_w = 2 * a.I; prm.I = a.I;
+  prm.out_gscale = a.out_gscale; prm.out_codes = a.out_codes; prm.out_sf = a.out_sf;
+  prm.c1_dbg = a.c1_dbg; prm.h_dbg = a.h_dbg;
+  constexpr int kWaves = 2;
+  prm.n_tiles = (a.I + 32 * kWaves - 1) / (32 * kWaves);
+  if (a.P >= 32 * a.E) return launch<kWaves, 2, 128, true>(prm, a.P, stream);
+  return launch<kWaves, 1, 128, true>(prm, a.P, stream);
 }
 
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream) {
   if (a.P == 0) return hipSuccess;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_kernel<false>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
-  const dim3 grid(a.H / kBN, m_tiles_bound(a.P, a.E));
-  hipLaunchKernelGGL(grouped_gemm_kernel<false>, grid, dim3(kThreads), kLdsBytes, stream,
-                     a.a_codes, a.a_sf, a.w_codes, a.w_sf, a.in_scale, a.w_scale2, a.offsets, a.E,
-                     a.I, a.H, a.I, a.out, a.H, (const float*)nullptr, (uint8_t*)nullptr,
-                     (uint8_t*)nullptr, (float*)nullptr, (uint16_t*)nullptr);
-  return hipGetLastError();
+  GemmParams prm{};
+  prm.a_codes = a.a_codes; prm.a_sf = a.a_sf; prm.w_codes = a.w_codes; prm.w_sf = a.w_sf;
+  prm.in_scale = a.in_scale; prm.w_scale2 = a.w_scale2; prm.offsets = a.offsets;
+  prm.E = a.E; prm.K = a.I; prm.N_w = a.H; prm.I = a.I;
+  prm.c_out = a.out; prm.ldc = a.H;
+  constexpr int kWaves = 4;
+  prm.n_tiles = (a.H + 64 * kWaves - 1) / (64 * kWaves);
+  if (a.P >= 32 * a.E) return launch<kWaves, 2, 64, false>(prm, a.P, stream);
+  return launch<kWaves, 1, 64, false>(prm, a.P, stream);
 }
 
 }  // namespace nvfp4

@@ -23,6 +23,8 @@ hipError_t launch_absmax(const uint16_t* x, int64_t ldx, int32_t K, const int32_
                          int32_t src_div, const int32_t* offsets, int32_t E, int32_t num_rows,
                          float* amax, hipStream_t stream);
 
+hipError_t launch_conversions_selftest(unsigned long long* count, hipStream_t stream);
+
 struct Gemm1Args {
   const uint8_t* a_codes;   // [P, H/2]
   const uint8_t* a_sf;      // [P, H/16]

@@ -124,4 +124,72 @@ hipError_t launch_absmax(const uint16_t* x, int64_t ldx, int32_t K, const int32_
   return hipGetLastError();
 }
 
+// Device self-check of the three conversion instructions the kernels rely
+// on, each against a reference built from the format definitions:
+//   count[0]: fp32 -> E2M1 encode (encode8) vs the midpoint comparisons of
+//             e2m1_code(), over every non-NaN fp32 pattern (each positive
+//             pattern and its negation form one pair);
+//   count[1]: E2M1 byte -> fp16 pair (GEMM operand dequant) vs the E2M1 table,
+//             all 256 bytes in all 4 byte positions, sign of zero included;
+//   count[2]: E4M3 byte -> fp16 (block-scale decode) vs e4m3_decode(), all
+//             256 codes except the two NaN patterns, in both halves.
+typedef _Float16 st_half2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float e2m1_ref(uint32_t c) {
+  const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+  const float v = mag[c & 7u];
+  return (c & 8u) ? -v : v;
+}
+
+__device__ __forceinline__ bool same_f16(_Float16 h, float ref) {
+  const float f = (float)h;
+  return f == ref && (__float_as_uint(f) >> 31) == (__float_as_uint(ref) >> 31);
+}
+
+__global__ __launch_bounds__(256) void conversions_selftest_kernel(unsigned long long* count) {
+  unsigned long long local = 0;
+  const uint32_t tid = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t u = tid; u < 0x80000000u; u += stride) {
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) continue;   // NaN
+    const float f[2] = {__uint_as_float(u), __uint_as_float(u | 0x80000000u)};
+    const uint32_t hw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, f[0], f[1], 1.0f, 0) & 0xFFu;
+    const uint32_t sw = e2m1_code(f[0]) | (e2m1_code(f[1]) << 4);
+    local += hw != sw;
+  }
+  if (local) atomicAdd(count, local);
+  if (tid < 256) {
+    const uint32_t b = tid;
+    unsigned long long bad = 0;
+    const st_half2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(b, 1.0f, 0);
+    const st_half2 d1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(b << 8, 1.0f, 1);
+    const st_half2 d2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(b << 16, 1.0f, 2);
+    const st_half2 d3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(b << 24, 1.0f, 3);
+    const st_half2 d[4] = {d0, d1, d2, d3};
+    for (int i = 0; i < 4; ++i)
+      bad += !same_f16(d[i].x, e2m1_ref(b & 15u)) + !same_f16(d[i].y, e2m1_ref(b >> 4));
+    if (bad) atomicAdd(count + 1, bad);
+    if ((b & 0x7Fu) != 0x7Fu) {
+      const float ref = (b & 0x80u) ? -e4m3_decode(b & 0x7Fu) : e4m3_decode(b);
+      const st_half2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b | (b << 8), 1.0f, false);
+      const st_half2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((b << 16) | (b << 24), 1.0f, true);
+      const unsigned long long bad8 = !same_f16(lo.x, ref) + !same_f16(lo.y, ref) +
+                                      !same_f16(hi.x, ref) + !same_f16(hi.y, ref);
+      if (bad8) atomicAdd(count + 2, bad8);
+    }
+  }
+}
+
+__global__ void zero_u64_kernel(unsigned long long* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
+}
+
+hipError_t launch_conversions_selftest(unsigned long long* count, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(64), 0, stream, count, 3);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(conversions_selftest_kernel, dim3(8192), dim3(256), 0, stream, count);
+  return hipGetLastError();
+}
+
 }  // namespace nvfp4

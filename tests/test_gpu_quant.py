@@ -126,3 +126,16 @@ def test_zero_rows_is_noop():
     L.quantize_experts(None, 16, 0, 16, 1, None, None, 1, None, codes, codes, 0)
     torch.cuda.synchronize()
     assert codes.cpu().numpy().tolist() == [[7] * 8]
+
+
+def test_hardware_conversions_selftest():
+    """The three conversion instructions behind the codes and the GEMM
+    operands equal references built from the format definitions: E2M1 encode
+    on every non-NaN fp32 input, E2M1 -> fp16 on every byte, E4M3 -> fp16 on
+    every non-NaN code."""
+    torch = _torch()
+    from nvfp4_w4a4_expert_amd import _lib as L
+    cnt = torch.full((3,), 12345, dtype=torch.int64, device="cuda")
+    L.selftest_conversions(cnt)
+    torch.cuda.synchronize()
+    assert cnt.cpu().tolist() == [0, 0, 0]
