@@ -206,15 +206,36 @@ NVFP4_API nvfp4_status_t nvfp4_selftest_conversions(unsigned long long* mismatch
                                                     nvfp4_stream_t stream);
 
 /*
+ * nvfp4_moe_pack_weights — load-time layout conversion of one projection's
+ * NVFP4 expert weights into the layout the grouped GEMMs read (page 3,
+ * "Kernel Backend": once the backend is chosen, the packed weights and their
+ * scales are converted to the layout that implementation requires, then
+ * handed to the kernel).  A pure byte permutation within each block of 32
+ * weight rows; sizes are unchanged.
+ *
+ *   projection  0 = w13 ([E, 2I, H]: codes [E, 2I, H/2], scales [E, 2I, H/16]),
+ *               1 = w2  ([E, H, I]:  codes [E, H, I/2],  scales [E, H, I/16]).
+ *   codes, sf   device, the checkpoint's row-major layout (16-byte aligned codes).
+ *   codes_out, sf_out  device, same sizes, distinct from the inputs: the
+ *               kernel layout nvfp4_moe_forward expects.
+ *   Requires H % 128 == 0 and I % 64 == 0 (else NVFP4_ERR_UNSUPPORTED).
+ */
+NVFP4_API nvfp4_status_t nvfp4_moe_pack_weights(int32_t projection, const uint8_t* codes,
+                                                const uint8_t* sf, int32_t num_experts,
+                                                int32_t hidden, int32_t inter, uint8_t* codes_out,
+                                                uint8_t* sf_out, nvfp4_stream_t stream);
+
+/*
  * One MoE layer's NVFP4 expert weights and scales — the checkpoint fields of
  * page 3 ("ROOT CAUSE" and the glossary's static weight quantisation entry:
  * w13/w2 packed FP4 weights, weight_scale (E4M3 per 16), weight_scale_2
  * (FP32 per expert), w13_input_scale / w2_input_scale (FP32 per expert)),
  * plus the reciprocals a1_gscale / a2_gscale from nvfp4_validate_scales.
- * All device pointers, caller-owned, logical PyTorch [out, in] layout:
- *   w13 [E, 2I, H/2] + w13_sf [E, 2I, H/16]: rows [0, I) gate, [I, 2I) up
- *   ("矩阵融合", gated FFN: gate and up fused into w13);
- *   w2 [E, H, I/2] + w2_sf [E, H, I/16];  *_scale2, *_input_scale, a*_gscale [E].
+ * All device pointers, caller-owned.  w13/w13_sf and w2/w2_sf are in the
+ * kernel layout produced by nvfp4_moe_pack_weights from the logical PyTorch
+ * [out, in] layout: w13 [E, 2I, H] with rows [0, I) gate and [I, 2I) up
+ * ("矩阵融合", gated FFN: gate and up fused into w13), w2 [E, H, I];
+ * *_scale2, *_input_scale, a*_gscale [E].
  */
 typedef struct {
   const uint8_t* w13;

@@ -62,6 +62,7 @@ _SIGS = {
     "nvfp4_permute": (_i32, [_p, _i32, _i32, _i32, _p, _p, _p, _p]),
     "nvfp4_expert_absmax": (_i32, [_p, _i64, _i32, _p, _i32, _p, _i32, _i32, _p, _p]),
     "nvfp4_selftest_conversions": (_i32, [_p, _p]),
+    "nvfp4_moe_pack_weights": (_i32, [_i32, _p, _p, _i32, _i32, _i32, _p, _p, _p]),
     "nvfp4_moe_workspace_size": (_i32, [_i32, _i32, ctypes.POINTER(MoEWeights), ctypes.POINTER(ctypes.c_size_t)]),
     "nvfp4_moe_forward": (_i32, [ctypes.POINTER(MoEWeights), _p, _p, _i32, _i32, _p, _p, _p,
                                  ctypes.c_size_t, ctypes.POINTER(MoEDebug), _p]),
@@ -152,6 +153,13 @@ def expert_absmax(x, ldx: int, K: int, src, src_div: int, expert_offsets, num_ex
 def selftest_conversions(mismatches, stream=None):
     _check(_lib.nvfp4_selftest_conversions(_ptr(mismatches), _stream(stream)),
            "nvfp4_selftest_conversions")
+
+
+def moe_pack_weights(projection: int, codes, sf, num_experts: int, hidden: int, inter: int,
+                     codes_out, sf_out, stream=None):
+    _check(_lib.nvfp4_moe_pack_weights(projection, _ptr(codes), _ptr(sf), num_experts, hidden,
+                                       inter, _ptr(codes_out), _ptr(sf_out), _stream(stream)),
+           "nvfp4_moe_pack_weights")
 
 
 def moe_workspace_size(num_tokens: int, k: int, weights: MoEWeights) -> int:

@@ -170,6 +170,23 @@ NVFP4_API nvfp4_status_t nvfp4_selftest_conversions(unsigned long long* mismatch
   return device_status(launch_conversions_selftest(mismatches, static_cast<hipStream_t>(stream)));
 }
 
+NVFP4_API nvfp4_status_t nvfp4_moe_pack_weights(int32_t projection, const uint8_t* codes,
+                                                const uint8_t* sf, int32_t num_experts,
+                                                int32_t hidden, int32_t inter, uint8_t* codes_out,
+                                                uint8_t* sf_out, nvfp4_stream_t stream) {
+  if (projection != 0 && projection != 1) return NVFP4_ERR_INVALID_ARG;
+  if (num_experts < 1 || hidden <= 0 || inter <= 0 || hidden % 16 || inter % 16)
+    return NVFP4_ERR_INVALID_ARG;
+  if (hidden % 128 || inter % 64) return NVFP4_ERR_UNSUPPORTED;
+  if (!codes || !sf || !codes_out || !sf_out || codes == codes_out || sf == sf_out)
+    return NVFP4_ERR_INVALID_ARG;
+  if (!aligned(codes, 16) || !aligned(codes_out, 16)) return NVFP4_ERR_INVALID_ARG;
+  const int32_t N = projection == 0 ? 2 * inter : hidden;
+  const int32_t K = projection == 0 ? hidden : inter;
+  return device_status(launch_pack_weights(projection, codes, sf, num_experts, N, K, codes_out,
+                                           sf_out, static_cast<hipStream_t>(stream)));
+}
+
 NVFP4_API nvfp4_status_t nvfp4_moe_workspace_size(int32_t num_tokens, int32_t k,
                                                   const nvfp4_moe_weights_t* w, size_t* bytes) {
   if (!bytes || !w || num_tokens < 0 || k < 1) return NVFP4_ERR_INVALID_ARG;

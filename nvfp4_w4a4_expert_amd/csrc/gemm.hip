@@ -57,6 +57,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kXcds = 8;
+constexpr int kMaxExperts = 1024;
 
 template <int V>
 using Int = std::integral_constant<int, V>;
@@ -80,50 +81,6 @@ __device__ __forceinline__ half2_t scales_f16(uint32_t w) {
 __device__ __forceinline__ half2_t bcast_lo(half2_t v) { return half2_t{v.x, v.x}; }
 __device__ __forceinline__ half2_t bcast_hi(half2_t v) { return half2_t{v.y, v.y}; }
 
-// Block-wide search of grouped m-tile `mt` (tiles of `bm` rows): false when
-// mt is past the last tile.  s_scan: 8 ints of LDS.  Threads own experts in
-// chunks of 4 * (1024 / blockDim) so any E <= 1024 is covered.
-template <int kThreads>
-__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int32_t E,
-                                          int32_t mt, int32_t bm, int32_t* s_scan,
-                                          int32_t& e_out, int32_t& row0, int32_t& rows) {
-  constexpr int kPer = 1024 / kThreads;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int32_t cnt[kPer], total = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int32_t e = kPer * tid + i;
-    const int32_t m = e < E ? offsets[e + 1] - offsets[e] : 0;
-    cnt[i] = (m + bm - 1) / bm;
-    total += cnt[i];
-  }
-  int32_t incl = total;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int32_t o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
-  if (lane == 63) s_scan[wave] = incl;
-  if (tid == 0) s_scan[6] = -1;
-  __syncthreads();
-  int32_t base = incl - total;
-  for (int w = 0; w < wave; ++w) base += s_scan[w];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    if (mt >= base && mt < base + cnt[i]) {
-      s_scan[6] = kPer * tid + i;
-      s_scan[7] = mt - base;
-    }
-    base += cnt[i];
-  }
-  __syncthreads();
-  if (s_scan[6] < 0) return false;
-  e_out = s_scan[6];
-  row0 = offsets[e_out] + s_scan[7] * bm;
-  rows = min(bm, offsets[e_out + 1] - row0);
-  return true;
-}
-
 struct GemmParams {
   const uint8_t* a_codes;   // [P, K/2]
   const uint8_t* a_sf;      // [P, K/16]
@@ -133,7 +90,7 @@ struct GemmParams {
   const float* w_scale2;    // [E]
   const int32_t* offsets;   // [E+1]
   int32_t E, K, N_w, I;     // N_w: weight rows per expert; I: GEMM1 h width
-  int32_t n_tiles, m_tiles_bound, grid_per_xcd;
+  int32_t n_tiles;
   // GEMM2 output
   float* c_out;             // [P, ldc]
   int32_t ldc;
@@ -148,7 +105,7 @@ struct GemmParams {
 }  // namespace
 
 template <int kWaves, int kMB, int kBK, bool kGated>
-__global__ __launch_bounds__(64 * kWaves) void grouped_gemm_kernel(const GemmParams prm) {
+__global__ __launch_bounds__(64 * kWaves, 2) void grouped_gemm_kernel(const GemmParams prm) {
   constexpr int kThreads = 64 * kWaves;
   constexpr int kBM = 32 * kMB;
   constexpr int kLdA = kBK + 8;                          // fp16 per LDS row (16-byte pad)
@@ -157,16 +114,68 @@ __global__ __launch_bounds__(64 * kWaves) void grouped_gemm_kernel(const GemmPar
   constexpr int kVec = kBK / 64;                         // 16-byte B loads per block per step
   constexpr int kSteps = kBK / 16;                       // MFMAs (per block pair) per step
   __shared__ __align__(16) _Float16 smem[2 * kBM * kLdA];
+  __shared__ int32_t s_off[kMaxExperts + 1];             // expert row offsets
+  __shared__ int32_t s_mt[kMaxExperts + 1];              // m-tiles before each expert
   __shared__ int32_t s_scan[8];
 
-  // XCD-aware remap of the hardware workgroup id to a logical tile id
-  const int32_t hw = blockIdx.x;
-  const int32_t logical = (hw % kXcds) * prm.grid_per_xcd + hw / kXcds;
+  // ---- once per workgroup: per-expert m-tile prefix in LDS -----------------
+  {
+    constexpr int kPer = (kMaxExperts + kThreads - 1) / kThreads;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int32_t cnt[kPer], total = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int32_t e = kPer * tid + i;
+      int32_t m = 0;
+      if (e < prm.E) {
+        const int32_t o0 = prm.offsets[e], o1 = prm.offsets[e + 1];
+        s_off[e] = o0;
+        if (e == prm.E - 1) s_off[prm.E] = o1;
+        m = o1 - o0;
+      }
+      cnt[i] = (m + kBM - 1) / kBM;
+      total += cnt[i];
+    }
+    int32_t incl = total;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_scan[wave] = incl;
+    __syncthreads();
+    int32_t base = incl - total;
+    for (int w = 0; w < wave; ++w) base += s_scan[w];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int32_t e = kPer * tid + i;
+      if (e <= prm.E) s_mt[e] = base;
+      base += cnt[i];
+    }
+    __syncthreads();
+  }
+  const int32_t total_m = s_mt[prm.E];
+  const int32_t total = total_m * prm.n_tiles;
+  const int32_t per_xcd = (total + kXcds - 1) / kXcds;
+
+  // ---- persistent loop over tiles; the workgroups on one XCD walk a
+  // contiguous range of (m-tile, n-tile) so they share that XCD's L2 --------
+  for (int32_t t = blockIdx.x; t < per_xcd * kXcds; t += gridDim.x) {
+  const int32_t logical = (t % kXcds) * per_xcd + t / kXcds;
+  if (logical >= total) continue;
   const int32_t mt = logical / prm.n_tiles;
   const int32_t nt = logical - mt * prm.n_tiles;
-  if (mt >= prm.m_tiles_bound) return;
-  int32_t e, row0, rows;
-  if (!find_tile<kThreads>(prm.offsets, prm.E, mt, kBM, s_scan, e, row0, rows)) return;
+  int32_t e = 0;
+  {
+    int32_t lo = 0, hi = prm.E - 1;                      // last e with s_mt[e] <= mt
+    while (lo < hi) {
+      const int32_t mid = (lo + hi + 1) >> 1;
+      if (s_mt[mid] <= mt) lo = mid; else hi = mid - 1;
+    }
+    e = lo;
+  }
+  const int32_t row0 = s_off[e] + (mt - s_mt[e]) * kBM;
+  const int32_t rows = min(kBM, s_off[e + 1] - row0);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t K = prm.K;
@@ -191,7 +200,11 @@ __global__ __launch_bounds__(64 * kWaves) void grouped_gemm_kernel(const GemmPar
   }
 
   // ---- B streaming assignment: wave's 64 weight rows, 2 blocks of 32 ------
-  // GEMM1: block 0 = gate rows, block 1 = the matching up rows.
+  // GEMM1: block 0 = gate rows, block 1 = the matching up rows.  Weights are
+  // in the kernel layout (nvfp4_moe_pack_weights): inside each 32-row block,
+  // K step kt holds, lane by lane, the 16-byte pieces each lane consumes, so a
+  // wavefront's load is one contiguous 1 KB per piece (plus 64 contiguous
+  // scale groups of kBK/32 bytes).
   const int32_t hc0 = kGated ? nt * (32 * kWaves) + 32 * wave : 0;   // h column base
   const int32_t n0 = kGated ? 0 : nt * (64 * kWaves) + 64 * wave;    // output column base
   const bool active = kGated ? hc0 < prm.I : n0 < prm.N_w;
@@ -200,13 +213,13 @@ __global__ __launch_bounds__(64 * kWaves) void grouped_gemm_kernel(const GemmPar
   const uint8_t* b_sp[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    int32_t wrow;
-    if (kGated) wrow = (j == 0 ? hc0 : prm.I + hc0) + (lane & 31);
-    else wrow = n0 + 32 * j + (lane & 31);
-    if (!active) wrow = 0;
-    const int64_t base = (int64_t)e * prm.N_w + wrow;
-    b_cp[j] = prm.w_codes + base * kb2 + (kBK / 4) * g;
-    b_sp[j] = prm.w_sf + base * kb16 + (kBK / 32) * g;
+    int32_t blk_row0;                                  // first row of the 32-row block
+    if (kGated) blk_row0 = j == 0 ? hc0 : prm.I + hc0;
+    else blk_row0 = n0 + 32 * j;
+    if (!active) blk_row0 = 0;                         // inactive waves read block 0
+    const int64_t rbase = (int64_t)e * prm.N_w + blk_row0;
+    b_cp[j] = prm.w_codes + rbase * kb2 + 16 * lane;
+    b_sp[j] = prm.w_sf + rbase * kb16 + (kBK / 32) * lane;
   }
 
   f32x16_t acc[kMB][2];
@@ -215,54 +228,59 @@ __global__ __launch_bounds__(64 * kWaves) void grouped_gemm_kernel(const GemmPar
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
 
-  u32x4 a_raw[kChunksPerThread];
-  uint32_t a_sraw[kChunksPerThread];
-  u32x4 b_raw[2][2][kVec];    // [buffer][block][16-byte piece]
-  uint32_t b_sraw[2][2];      // [buffer][block]: kBK/32 scale bytes
+  // Register rings (3 slots) for the packed codes of A and B: step kt's
+  // loads are issued two steps before their use.
+  constexpr int kRing = 3;
+  u32x4 a_raw[kRing][kChunksPerThread];
+  uint32_t a_sraw[kRing][kChunksPerThread];
+  u32x4 b_raw[kRing][2][kVec];    // [slot][block][16-byte piece]
+  uint32_t b_sraw[kRing][2];      // [slot][block]: kBK/32 scale bytes
 
-  auto load_a = [&](int kt) {
+  auto load_a = [&](int kt, auto slotc) {
+    constexpr int slot = decltype(slotc)::value;
 #pragma unroll
     for (int i = 0; i < kChunksPerThread; ++i) {
       if (!a_on[i]) continue;
-      a_raw[i] = *reinterpret_cast<const u32x4*>(a_cp[i] + (int64_t)kt * (kBK / 2));
-      a_sraw[i] = *reinterpret_cast<const uint16_t*>(a_sp[i] + (int64_t)kt * (kBK / 16));
+      a_raw[slot][i] = *reinterpret_cast<const u32x4*>(a_cp[i] + (int64_t)kt * (kBK / 2));
+      a_sraw[slot][i] = *reinterpret_cast<const uint16_t*>(a_sp[i] + (int64_t)kt * (kBK / 16));
     }
   };
-  auto store_a = [&](auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
+  // dequantise the A step held in register slot `slot` into LDS buffer `buf`
+  auto store_a = [&](int buf, auto slotc) {
+    constexpr int slot = decltype(slotc)::value;
     _Float16* base = smem + buf * (kBM * kLdA);
 #pragma unroll
     for (int i = 0; i < kChunksPerThread; ++i) {
       if (!a_on[i]) continue;
-      const half2_t sp = scales_f16<false>(a_sraw[i]);
+      const half2_t sp = scales_f16<false>(a_sraw[slot][i]);
       const half2_t s0 = bcast_lo(sp), s1 = bcast_hi(sp);
       half8_t* dst = reinterpret_cast<half8_t*>(base + a_lds[i]);
-      dst[0] = dequant8(a_raw[i].x, s0);
-      dst[1] = dequant8(a_raw[i].y, s0);
-      dst[2] = dequant8(a_raw[i].z, s1);
-      dst[3] = dequant8(a_raw[i].w, s1);
+      dst[0] = dequant8(a_raw[slot][i].x, s0);
+      dst[1] = dequant8(a_raw[slot][i].y, s0);
+      dst[2] = dequant8(a_raw[slot][i].z, s1);
+      dst[3] = dequant8(a_raw[slot][i].w, s1);
     }
   };
-  auto load_b = [&](int kt, auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
+  auto load_b = [&](int kt, auto slotc) {
+    constexpr int buf = decltype(slotc)::value;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(b_cp[j] + (int64_t)kt * (kBK / 2));
+      const uint8_t* cbase = b_cp[j] + (int64_t)kt * (kVec * 1024);
 #pragma unroll
-      for (int v = 0; v < kVec; ++v) b_raw[buf][j][v] = src[v];
-      const uint8_t* sp = b_sp[j] + (int64_t)kt * (kBK / 16);
+      for (int v = 0; v < kVec; ++v)
+        b_raw[buf][j][v] = *reinterpret_cast<const u32x4*>(cbase + 1024 * v);
+      const uint8_t* sp = b_sp[j] + (int64_t)kt * (64 * (kBK / 32));
       if constexpr (kBK == 128) b_sraw[buf][j] = *reinterpret_cast<const uint32_t*>(sp);
       else b_sraw[buf][j] = *reinterpret_cast<const uint16_t*>(sp);
     }
   };
-  // One K step: kSteps MFMA rounds of (kMB x 2) 32x32x16 products.  The
-  // operands of round s+1 (B dequantised from registers, A read from LDS) are
-  // produced while round s's MFMAs run; the scheduling groups below interleave
-  // one MFMA with the next round's conversions and LDS reads so the matrix
-  // core is fed from a single wavefront.
-  auto compute = [&](auto bufc) {
+  // One K step: kSteps MFMA rounds of (kMB x 2) 32x32x16 products on LDS
+  // buffer `lbuf` and B ring slot `buf`.  The operands of round s+1 (B
+  // dequantised from registers, A read from LDS) are produced while round
+  // s's MFMAs run.
+  auto compute = [&](int lbuf, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    const _Float16* abase = smem + buf * (kBM * kLdA) + (lane & 31) * kLdA + (kBK / 2) * g;
+    const _Float16* abase = smem + lbuf * (kBM * kLdA) + (lane & 31) * kLdA + (kBK / 2) * g;
     // block scales of this step: kBK/32 per block, as fp16 pairs
     half2_t sc[2][2];
 #pragma unroll
@@ -300,12 +318,6 @@ __global__ __launch_bounds__(64 * kWaves) void grouped_gemm_kernel(const GemmPar
       }
       if (st + 1 < kSteps) {
 #pragma unroll
-        for (int m = 0; m < 2 * kMB; ++m) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 8 / kMB, 0); // next round's conversions
-          if (m < kMB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-        }
-#pragma unroll
         for (int j = 0; j < 2; ++j) bf[j] = nbf[j];
 #pragma unroll
         for (int i = 0; i < kMB; ++i) af[i] = naf[i];
@@ -313,34 +325,42 @@ __global__ __launch_bounds__(64 * kWaves) void grouped_gemm_kernel(const GemmPar
     }
   };
 
-  // ---- pipeline: step kt runs the MFMAs on buffer kt&1 while A(kt+1) is
-  // dequantised into the other LDS buffer and A(kt+2), B(kt+2) are in flight.
-  // Full pairs of steps run in a loop with no early exit (so the accumulators
-  // stay in place); an odd last step follows it.
-  load_a(0);
+  // ---- pipeline.  Ring slot of step x is x % 3; LDS buffer is x & 1.
+  // Step kt: issue A(kt+3) into the slot A(kt) left; in one basic block
+  // dequantise A(kt+1) into LDS buffer (kt+1)&1 and run the MFMAs of step kt
+  // (LDS buffer kt&1, B slot kt%3) so the scheduler interleaves them; issue
+  // B(kt+3) into the slot just consumed; one barrier.  Whole groups of three
+  // steps loop with no early exit (so accumulators stay in place); the last
+  // one or two steps follow.
+  load_a(0, Int<0>{});
+  if (nk > 1) load_a(1, Int<1>{});
+  if (nk > 2) load_a(2, Int<2>{});
   load_b(0, Int<0>{});
-  store_a(Int<0>{});
-  if (nk > 1) {
-    load_a(1);
-    load_b(1, Int<1>{});
-  }
+  if (nk > 1) load_b(1, Int<1>{});
+  if (nk > 2) load_b(2, Int<2>{});
+  store_a(0, Int<0>{});
   __syncthreads();
   auto step = [&](int kt, auto rc) {
     constexpr int r = decltype(rc)::value;
-    compute(Int<r>{});
-    if (kt + 1 < nk) store_a(Int<r ^ 1>{});
-    if (kt + 2 < nk) {
-      load_a(kt + 2);
-      load_b(kt + 2, Int<r>{});
+    constexpr int rn = (r + 1) % kRing;
+    if (kt + 3 < nk) load_a(kt + 3, Int<r>{});
+    if (active) {
+      store_a((kt + 1) & 1, Int<rn>{});
+      compute(kt & 1, Int<r>{});
+    } else {
+      store_a((kt + 1) & 1, Int<rn>{});
     }
+    if (kt + 3 < nk) load_b(kt + 3, Int<r>{});
     __syncthreads();
   };
-  const int nk2 = nk & ~1;
-  for (int kt = 0; kt < nk2; kt += 2) {
+  const int nk3 = nk - nk % 3;
+  for (int kt = 0; kt < nk3; kt += 3) {
     step(kt, Int<0>{});
     step(kt + 1, Int<1>{});
+    step(kt + 2, Int<2>{});
   }
-  if (nk2 < nk) step(nk2, Int<0>{});
+  if (nk3 < nk) step(nk3, Int<0>{});
+  if (nk3 + 1 < nk) step(nk3 + 1, Int<1>{});
 
   const float alpha = prm.in_scale[e] * prm.w_scale2[e];
   // MFMA 32x32 output layout: lane holds column (lane & 31) and rows
@@ -348,7 +368,7 @@ __global__ __launch_bounds__(64 * kWaves) void grouped_gemm_kernel(const GemmPar
   const int ccol = lane & 31, crow = 4 * g;
 
   if constexpr (!kGated) {
-    if (!active) return;
+    if (active)
 #pragma unroll
     for (int mi = 0; mi < kMB; ++mi)
 #pragma unroll
@@ -413,6 +433,8 @@ __global__ __launch_bounds__(64 * kWaves) void grouped_gemm_kernel(const GemmPar
       }
     }
   }
+  __syncthreads();   // LDS is reused by the next tile
+  }
 }
 
 namespace {
@@ -421,13 +443,30 @@ int32_t m_tiles_bound(int32_t P, int32_t E, int32_t bm) {
   return (P + bm - 1) / bm + (P < E ? P : E);
 }
 
+// Resident workgroups per CU for a kernel, and the CU count, looked up once
+// per process for the current device.
+struct Residency {
+  int cus = 0, per_cu = 0;
+};
+
 template <int kWaves, int kMB, int kBK, bool kGated>
 hipError_t launch(GemmParams prm, int32_t P, hipStream_t stream) {
   constexpr int kBM = 32 * kMB;
-  prm.m_tiles_bound = m_tiles_bound(P, prm.E, kBM);
-  const int64_t tiles = (int64_t)prm.m_tiles_bound * prm.n_tiles;
-  prm.grid_per_xcd = (int32_t)((tiles + kXcds - 1) / kXcds);
-  const int64_t grid = (int64_t)prm.grid_per_xcd * kXcds;
+  static Residency res;
+  if (res.cus == 0) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&res.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err == hipSuccess)
+      err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &res.per_cu, (const void*)grouped_gemm_kernel<kWaves, kMB, kBK, kGated>, 64 * kWaves, 0);
+    if (err != hipSuccess) return err;
+    if (res.per_cu < 1) res.per_cu = 1;
+  }
+  const int64_t tiles = (int64_t)m_tiles_bound(P, prm.E, kBM) * prm.n_tiles;
+  const int64_t slots = (int64_t)res.cus * res.per_cu;
+  int64_t grid = tiles < slots ? tiles : slots;
+  grid = (grid + kXcds - 1) / kXcds * kXcds;            // whole XCD rounds
   hipLaunchKernelGGL((grouped_gemm_kernel<kWaves, kMB, kBK, kGated>), dim3((uint32_t)grid),
                      dim3(64 * kWaves), 0, stream, prm);
   return hipGetLastError();
@@ -445,7 +484,7 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream) {
   prm.E = a.E; prm.K = a.H; prm.N_w = 2 * a.I; prm.I = a.I;
   prm.out_gscale = a.out_gscale; prm.out_codes = a.out_codes; prm.out_sf = a.out_sf;
   prm.c1_dbg = a.c1_dbg; prm.h_dbg = a.h_dbg;
-  constexpr int kWaves = 2;
+  constexpr int kWaves = 4;
   prm.n_tiles = (a.I + 32 * kWaves - 1) / (32 * kWaves);
   if (a.P >= 32 * a.E) return launch<kWaves, 2, 128, true>(prm, a.P, stream);
   return launch<kWaves, 1, 128, true>(prm, a.P, stream);
@@ -462,6 +501,68 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream) {
   prm.n_tiles = (a.H + 64 * kWaves - 1) / (64 * kWaves);
   if (a.P >= 32 * a.E) return launch<kWaves, 2, 64, false>(prm, a.P, stream);
   return launch<kWaves, 1, 64, false>(prm, a.P, stream);
+}
+
+// ---- load-time weight layout conversion -----------------------------------
+// Checkpoint layout: codes [E][N][K/2], scales [E][N][K/16], row-major.
+// Kernel layout (same sizes): for each expert e, 32-row block nb and K step
+// ks (kBK wide), the codes are stored lane by lane as the wavefront reads
+// them: piece (v, lane) = 16 bytes of row nb*32 + (lane & 31), elements
+// ks*kBK + (lane >> 5)*kBK/2 + 32v + [0, 32); the scales likewise hold, for
+// each lane, the kBK/32 block scales of that row and K range.
+__global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t* __restrict__ src,
+                                                         uint8_t* __restrict__ dst, int64_t pieces,
+                                                         int32_t N, int32_t K, int32_t bk) {
+  const int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gi >= pieces) return;
+  const int32_t kvec = bk / 64, nks = K / bk, nb_per = N / 32;
+  const int32_t lane = (int32_t)(gi % 64);
+  int64_t t = gi / 64;
+  const int32_t v = (int32_t)(t % kvec);
+  t /= kvec;
+  const int32_t ks = (int32_t)(t % nks);
+  t /= nks;
+  const int32_t nb = (int32_t)(t % nb_per);
+  const int64_t e = t / nb_per;
+  const int64_t row = e * N + nb * 32 + (lane & 31);
+  const int64_t k0 = (int64_t)ks * bk + (lane >> 5) * (bk / 2) + 32 * v;
+  *reinterpret_cast<uint4*>(dst + gi * 16) =
+      *reinterpret_cast<const uint4*>(src + row * (K / 2) + k0 / 2);
+}
+
+__global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restrict__ src,
+                                                          uint8_t* __restrict__ dst, int64_t items,
+                                                          int32_t N, int32_t K, int32_t bk) {
+  const int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gi >= items) return;
+  const int32_t nks = K / bk, nb_per = N / 32, per = bk / 32;
+  const int32_t lane = (int32_t)(gi % 64);
+  int64_t t = gi / 64;
+  const int32_t ks = (int32_t)(t % nks);
+  t /= nks;
+  const int32_t nb = (int32_t)(t % nb_per);
+  const int64_t e = t / nb_per;
+  const int64_t row = e * N + nb * 32 + (lane & 31);
+  const int64_t blk = ((int64_t)ks * bk + (lane >> 5) * (bk / 2)) / 16;
+  for (int32_t i = 0; i < per; ++i) dst[gi * per + i] = src[row * (K / 16) + blk + i];
+}
+
+int32_t weight_step_k(int32_t projection) { return projection == 0 ? 128 : 64; }
+
+hipError_t launch_pack_weights(int32_t projection, const uint8_t* codes, const uint8_t* sf,
+                               int32_t E, int32_t N, int32_t K, uint8_t* codes_out,
+                               uint8_t* sf_out, hipStream_t stream) {
+  const int32_t bk = weight_step_k(projection);
+  const int64_t pieces = (int64_t)E * N * K / 32;        // 16-byte pieces
+  const int64_t items = (int64_t)E * (N / 32) * (K / bk) * 64;
+  if (pieces == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_codes_kernel, dim3((uint32_t)((pieces + 255) / 256)), dim3(256), 0,
+                     stream, codes, codes_out, pieces, N, K, bk);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(pack_scales_kernel, dim3((uint32_t)((items + 255) / 256)), dim3(256), 0,
+                     stream, sf, sf_out, items, N, K, bk);
+  return hipGetLastError();
 }
 
 }  // namespace nvfp4

@@ -54,6 +54,9 @@ struct Gemm2Args {
 };
 
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream);
+hipError_t launch_pack_weights(int32_t projection, const uint8_t* codes, const uint8_t* sf,
+                               int32_t E, int32_t N, int32_t K, uint8_t* codes_out,
+                               uint8_t* sf_out, hipStream_t stream);
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream);
 
 hipError_t launch_combine(const float* c2, const float* w, const int32_t* inv, int32_t T,

@@ -56,10 +56,12 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
 class NVFP4MoELayer:
     """Device-resident NVFP4 MoE layer.
 
-    Weight tensors may be numpy arrays (uploaded) or device tensors (used in
-    place): w13 [E, 2I, H/2] u8, w13_sf [E, 2I, H/16] u8, w13_scale2 [E] f32,
-    w2 [E, H, I/2] u8, w2_sf [E, H, I/16] u8, w2_scale2 [E] f32.  The input
-    scales and `written` masks are host arrays; they are checked first.
+    Weight tensors may be numpy arrays (uploaded) or device tensors, in the
+    checkpoint layout: w13 [E, 2I, H/2] u8, w13_sf [E, 2I, H/16] u8,
+    w13_scale2 [E] f32, w2 [E, H, I/2] u8, w2_sf [E, H, I/16] u8, w2_scale2
+    [E] f32.  The input scales and `written` masks are host arrays; they are
+    checked first.  Codes and block scales are then converted once into the
+    kernel layout (nvfp4_moe_pack_weights); the inputs are left untouched.
     """
 
     def __init__(self, w13, w13_sf, w13_scale2, w2, w2_sf, w2_scale2,
@@ -75,15 +77,20 @@ class NVFP4MoELayer:
             raise BadScaleError("w2", slots)
         up8 = (lambda a: a if isinstance(a, torch.Tensor) else _dev_u8(a, device))
         up32 = (lambda a: a if isinstance(a, torch.Tensor) else _dev_f32(a, device))
-        self.w13, self.w13_sf, self.w13_scale2 = up8(w13), up8(w13_sf), up32(w13_scale2)
-        self.w2, self.w2_sf, self.w2_scale2 = up8(w2), up8(w2_sf), up32(w2_scale2)
+        w13, w13_sf, w2, w2_sf = up8(w13), up8(w13_sf), up8(w2), up8(w2_sf)
+        self.E = int(w13.shape[0])
+        self.I = int(w13.shape[1]) // 2
+        self.H = int(w13.shape[2]) * 2
+        # load-time layout conversion into the grouped GEMMs' kernel layout
+        self.w13, self.w13_sf = torch.empty_like(w13), torch.empty_like(w13_sf)
+        self.w2, self.w2_sf = torch.empty_like(w2), torch.empty_like(w2_sf)
+        _lib.moe_pack_weights(0, w13, w13_sf, self.E, self.H, self.I, self.w13, self.w13_sf)
+        _lib.moe_pack_weights(1, w2, w2_sf, self.E, self.H, self.I, self.w2, self.w2_sf)
+        self.w13_scale2, self.w2_scale2 = up32(w13_scale2), up32(w2_scale2)
         self.w13_input_scale = _dev_f32(s13, device)
         self.w2_input_scale = _dev_f32(s2, device)
         self.a1_gscale = _dev_f32(gs1, device)
         self.a2_gscale = _dev_f32(gs2, device)
-        self.E = int(self.w13.shape[0])
-        self.I = int(self.w13.shape[1]) // 2
-        self.H = int(self.w13.shape[2]) * 2
         self.device = device
         self._ws = None
 

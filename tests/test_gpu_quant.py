@@ -139,3 +139,50 @@ def test_hardware_conversions_selftest():
     L.selftest_conversions(cnt)
     torch.cuda.synchronize()
     assert cnt.cpu().tolist() == [0, 0, 0]
+
+
+def _pack_reference(codes, sf, bk):
+    """The kernel weight layout, stated directly: for expert e, 32-row block
+    nb and K step ks, lane l's 16-byte pieces v hold row nb*32 + (l & 31),
+    elements ks*bk + (l >> 5)*bk/2 + 32v + [0, 32); its scales hold the bk/32
+    block scales of that row and K range."""
+    E, N, Kh = codes.shape
+    K = Kh * 2
+    kvec, nks = bk // 64, K // bk
+    out_c = np.empty(E * N * K // 2, dtype=np.uint8)
+    out_s = np.empty(E * N * K // 16, dtype=np.uint8)
+    lanes = np.arange(64)
+    pc = ps = 0
+    for e in range(E):
+        for nb in range(N // 32):
+            rows = nb * 32 + (lanes & 31)
+            for ks in range(nks):
+                for v in range(kvec):
+                    k0 = ks * bk + (lanes >> 5) * (bk // 2) + 32 * v
+                    for l in range(64):
+                        out_c[pc:pc + 16] = codes[e, rows[l], k0[l] // 2:k0[l] // 2 + 16]
+                        pc += 16
+                b0 = (ks * bk + (lanes >> 5) * (bk // 2)) // 16
+                for l in range(64):
+                    out_s[ps:ps + bk // 32] = sf[e, rows[l], b0[l]:b0[l] + bk // 32]
+                    ps += bk // 32
+    return out_c, out_s
+
+
+@pytest.mark.parametrize("projection", [0, 1])
+def test_weight_packing_layout(projection):
+    """nvfp4_moe_pack_weights is the stated byte permutation, bit for bit."""
+    torch = _torch()
+    from nvfp4_w4a4_expert_amd import _lib as L
+    rng = np.random.default_rng(40 + projection)
+    E, H, I = 3, 256, 128
+    N, K = (2 * I, H) if projection == 0 else (H, I)
+    codes = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    sf = rng.integers(0, 0x7F, size=(E, N, K // 16), dtype=np.uint8)
+    dc, ds = torch.from_numpy(codes).cuda(), torch.from_numpy(sf).cuda()
+    oc, osf = torch.empty_like(dc), torch.empty_like(ds)
+    L.moe_pack_weights(projection, dc, ds, E, H, I, oc, osf)
+    torch.cuda.synchronize()
+    rc, rs = _pack_reference(codes, sf, 128 if projection == 0 else 64)
+    assert np.array_equal(oc.cpu().numpy().reshape(-1), rc)
+    assert np.array_equal(osf.cpu().numpy().reshape(-1), rs)
