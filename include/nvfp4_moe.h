@@ -158,9 +158,12 @@ NVFP4_API nvfp4_status_t nvfp4_route_topk(const float* logits, int32_t num_token
  * every expert's rows are contiguous for the grouped GEMMs (page 3,
  * "矩阵融合", MoE FFN paragraph: the backend reorders inputs by routing so
  * the per-expert products form one grouped GEMM).  The order is stable:
- * sorted by (expert, token, slot).  Deterministic, no atomics.
+ * sorted by (expert, token, slot).  Deterministic: the result does not depend
+ * on the order in which the device's threads run.
  *
- *   ids             device int32 [num_tokens*k], each in [0, num_experts).
+ *   ids             device int32 [num_tokens*k], each in [0, num_experts);
+ *                   pairs with an id outside that range are left out (their
+ *                   inv_pair entry is not written).  1 <= num_experts <= 1024.
  *   expert_offsets  device int32 [num_experts+1]: rows of expert e are
  *                   [offsets[e], offsets[e+1]).
  *   src_pair        device int32 [num_tokens*k]: permuted row p -> pair q.

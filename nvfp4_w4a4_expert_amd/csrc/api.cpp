@@ -143,6 +143,7 @@ NVFP4_API nvfp4_status_t nvfp4_permute(const int32_t* ids, int32_t num_tokens, i
                                        int32_t* src_pair, int32_t* inv_pair,
                                        nvfp4_stream_t stream) {
   if (num_tokens < 0 || k < 1 || num_experts < 1) return NVFP4_ERR_INVALID_ARG;
+  if (num_experts > 1024) return NVFP4_ERR_UNSUPPORTED;
   if (!expert_offsets) return NVFP4_ERR_INVALID_ARG;
   if (num_tokens > 0 && (!ids || !src_pair || !inv_pair)) return NVFP4_ERR_INVALID_ARG;
   if ((int64_t)num_tokens * k > 0x7FFFFFFF) return NVFP4_ERR_UNSUPPORTED;

@@ -11,10 +11,9 @@
 // descending, expert index ascending), pick the experts; the k weights are a
 // softmax over the picked logits in fp32.
 //
-// permute: one workgroup per expert.  Each thread owns a contiguous segment
-// of the pair array, so a block-wide exclusive scan of per-thread match
-// counts gives every match its stable rank (token-major order) without
-// atomics; the count of smaller expert ids gives the expert's offset.
+// permute: workgroups own consecutive blocks of pairs; each histograms all
+// ids, derives the expert offsets, and ranks its block's pairs stably with
+// wavefront ballots (see permute_kernel).
 #include <float.h>
 
 #include "internal.h"
@@ -96,8 +95,14 @@ hipError_t launch_route(const float* logits, int32_t T, int32_t E, int32_t k, in
   return hipGetLastError();
 }
 
-// Block-wide exclusive scan of one int per thread (256 threads).
-__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* total, int32_t* s_tmp) {
+constexpr int kPermThreads = 512;                 // 8 wavefronts
+constexpr int kPermWaves = kPermThreads / 64;
+constexpr int kPermMaxE = 1024;
+
+// Exclusive scan over the workgroup of one int per thread; *total receives
+// the sum.  s_tmp holds kPermWaves ints.
+__device__ __forceinline__ int32_t perm_exclusive_scan(int32_t v, int32_t* total,
+                                                       int32_t* s_tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int32_t incl = v;
 #pragma unroll
@@ -109,7 +114,7 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* tota
   __syncthreads();
   int32_t base = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < kPermWaves; ++w) {
     const int32_t s = s_tmp[w];
     base += w < wave ? s : 0;
     tot += s;
@@ -119,43 +124,129 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* tota
   return base + incl - v;
 }
 
-__global__ __launch_bounds__(256) void permute_kernel(const int32_t* __restrict__ ids, int32_t P,
-                                                      int32_t E, int32_t* __restrict__ offsets,
-                                                      int32_t* __restrict__ src_pair,
-                                                      int32_t* __restrict__ inv) {
-  __shared__ int32_t s_tmp[4];
-  const int32_t e = blockIdx.x;
-  const int32_t seg = (P + 255) / 256;
-  const int32_t q0 = min(P, (int32_t)threadIdx.x * seg);
-  const int32_t q1 = min(P, q0 + seg);
-  int32_t less = 0, eq = 0;
-  for (int32_t q = q0; q < q1; ++q) {
-    const int32_t id = ids[q];
-    less += id < e;
-    eq += id == e;
+// One workgroup per block of `span` consecutive pairs.
+//  1. Every workgroup histograms all P ids in LDS, split into pairs before
+//     its block and pairs from its block on; the counts are the same in
+//     every workgroup whatever the order of the LDS additions.
+//  2. An exclusive scan over experts of the totals gives expert offsets;
+//     adding the counts before the block gives each expert's first row in
+//     this block.
+//  3. The block's pairs are walked in token-major order, 512 at a time.
+//     Inside a wavefront, lanes holding the same expert are found with one
+//     ballot per id bit; a lane's rank among them is the popcount of the
+//     equal lanes below it.  Per-expert counts of the 8 wavefronts are
+//     turned into running bases by one thread per expert, so ranks follow
+//     pair order across wavefronts and across steps: the result is the
+//     stable order.
+// Ids outside [0, E) are left out of every count and never written.
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(
+    const int32_t* __restrict__ ids, int32_t P, int32_t E, int32_t id_bits, int32_t span,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ src_pair, int32_t* __restrict__ inv) {
+  __shared__ int32_t s_before[kPermMaxE];
+  __shared__ int32_t s_after[kPermMaxE];
+  __shared__ int32_t s_base[kPermMaxE];
+  __shared__ int32_t s_wave[kPermWaves][kPermMaxE];
+  __shared__ int32_t s_tmp[kPermWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t q0 = (int32_t)blockIdx.x * span;
+  const int32_t q1 = min(P, q0 + span);
+
+  for (int e = tid; e < E; e += kPermThreads) {
+    s_before[e] = 0;
+    s_after[e] = 0;
+#pragma unroll
+    for (int w = 0; w < kPermWaves; ++w) s_wave[w][e] = 0;
   }
-  int32_t total_less, total_eq;
-  (void)block_exclusive_scan(less, &total_less, s_tmp);
-  const int32_t rank0 = block_exclusive_scan(eq, &total_eq, s_tmp);
-  if (threadIdx.x == 0) {
-    offsets[e] = total_less;
-    if (e == E - 1) offsets[E] = total_less + total_eq;
+  __syncthreads();
+
+  // 1. histogram of all pairs
+  constexpr int kUnroll = 8;
+  for (int64_t qb = 0; qb < P; qb += kPermThreads * kUnroll) {
+    int32_t id[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t q = qb + u * kPermThreads + tid;
+      id[u] = q < P ? ids[q] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t q = qb + u * kPermThreads + tid;
+      if ((uint32_t)id[u] < (uint32_t)E) atomicAdd(q < q0 ? &s_before[id[u]] : &s_after[id[u]], 1);
+    }
   }
-  if (eq == 0) return;
-  int32_t p = total_less + rank0;
-  for (int32_t q = q0; q < q1; ++q) {
-    if (ids[q] == e) {
+  __syncthreads();
+
+  // 2. expert offsets; running base of each expert at the start of the block
+  const int per = (E + kPermThreads - 1) / kPermThreads;   // experts per thread (<= 2)
+  int32_t local = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < E) local += s_before[e] + s_after[e];
+  }
+  int32_t total;
+  int32_t run = perm_exclusive_scan(local, &total, s_tmp);
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < E) {
+      if (blockIdx.x == 0) offsets[e] = run;
+      s_base[e] = run + s_before[e];
+      run += s_before[e] + s_after[e];
+    }
+  }
+  if (blockIdx.x == 0 && tid == 0) offsets[E] = total;
+  __syncthreads();
+
+  // 3. stable ranks inside the block
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int64_t qs = q0; qs < q1; qs += kPermThreads) {
+    const int32_t q = (int32_t)min(qs + tid, (int64_t)q1);
+    const int32_t id = q < q1 ? ids[q] : -1;
+    const bool valid = (uint32_t)id < (uint32_t)E;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < id_bits; ++b) {
+      const bool bit = (id >> b) & 1;
+      const uint64_t ones = __ballot(bit);
+      same &= bit ? ones : ~ones;
+    }
+    const bool leader = valid && (same & below) == 0;
+    if (leader) s_wave[wave][id] = __popcll(same);
+    __syncthreads();
+    for (int e = tid; e < E; e += kPermThreads) {
+      int32_t r = s_base[e];
+#pragma unroll
+      for (int w = 0; w < kPermWaves; ++w) {
+        const int32_t c = s_wave[w][e];
+        if (c != 0) s_wave[w][e] = r;
+        r += c;
+      }
+      s_base[e] = r;
+    }
+    __syncthreads();
+    if (valid) {
+      const int32_t p = s_wave[wave][id] + __popcll(same & below);
       src_pair[p] = q;
       inv[q] = p;
-      ++p;
     }
+    // Only this wavefront touches row `wave` of s_wave until the next
+    // barrier, and its LDS operations complete in program order, so the
+    // leader clears its entry after every lane of the wavefront has read it.
+    if (leader) s_wave[wave][id] = 0;
   }
 }
 
 hipError_t launch_permute(const int32_t* ids, int32_t P, int32_t E, int32_t* offsets,
                           int32_t* src_pair, int32_t* inv, hipStream_t stream) {
-  hipLaunchKernelGGL(permute_kernel, dim3(E), dim3(256), 0, stream, ids, P, E, offsets, src_pair,
-                     inv);
+  if (E < 1 || E > kPermMaxE || P < 0) return hipErrorInvalidValue;
+  // Blocks of at least 2048 pairs; at most 256 of them, so the all-pairs
+  // histogram each workgroup builds stays a small multiple of P.
+  int64_t span = ((int64_t)P + 255) / 256;
+  span = (span + kPermThreads - 1) / kPermThreads * kPermThreads;
+  if (span < 2048) span = 2048;
+  const int32_t blocks = P == 0 ? 1 : (int32_t)(((int64_t)P + span - 1) / span);
+  int32_t id_bits = 0;
+  while ((1 << id_bits) < E) ++id_bits;
+  hipLaunchKernelGGL(permute_kernel, dim3(blocks), dim3(kPermThreads), 0, stream, ids, P, E,
+                     id_bits, (int32_t)span, offsets, src_pair, inv);
   return hipGetLastError();
 }
 

@@ -54,9 +54,33 @@ def test_zipf_stack_router_has_empty_experts(layer):
 
 
 @pytest.mark.parametrize("T,E,k", [(1, 4, 1), (3, 4, 4), (100, 64, 8), (50, 200, 32),
-                                   (9, 1000, 8), (33, 1024, 2), (257, 128, 8)])
+                                   (9, 1000, 8), (33, 1024, 2), (257, 128, 8),
+                                   (1000, 1024, 32), (4097, 4, 1), (6000, 7, 3)])
 def test_shapes_and_ties(T, E, k):
     rng = np.random.default_rng(T * 1000 + E)
     logits = rng.integers(-2, 3, size=(T, E)).astype(np.float32)   # heavy ties
     _check(logits, k)
     _check(rng.standard_normal((T, E)).astype(np.float32), k)
+
+
+def test_permute_many_blocks_skewed():
+    """131072 pairs (several permutation blocks, the last one ragged), most of
+    them on a few experts, others on none: offsets, src_pair, inv bit-exact."""
+    rng = np.random.default_rng(77)
+    T, E, k = 16385, 256, 8
+    p = np.exp(-0.05 * np.arange(E))
+    p[100:140] = 0.0
+    p /= p.sum()
+    ids = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    import torch
+    from nvfp4_w4a4_expert_amd import _lib as L
+    d_ids = torch.from_numpy(ids).cuda()
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    src = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    inv = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    L.permute(d_ids, T, k, E, off, src, inv)
+    torch.cuda.synchronize()
+    roff, rsrc, rinv = OM.permute(ids, E)
+    assert np.array_equal(off.cpu().numpy(), roff)
+    assert np.array_equal(src.cpu().numpy(), rsrc)
+    assert np.array_equal(inv.cpu().numpy(), rinv)
