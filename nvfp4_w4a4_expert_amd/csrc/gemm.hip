@@ -57,6 +57,22 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kXcds = 8;
+
+#ifndef GEMM_SIMPLE_ROUNDS
+#define GEMM_SIMPLE_ROUNDS 0
+#endif
+#ifndef GEMM_ROUND_BARRIER
+#define GEMM_ROUND_BARRIER 0
+#endif
+#ifndef G1_MB
+#define G1_MB 2
+#define G1_BK 128
+#define G1_RING 3
+#define G1_OCC 2
+#define G2_MB 4
+#define G2_RING 2
+#define G2_OCC 2
+#endif
 constexpr int kMaxExperts = 1024;
 
 template <int V>
@@ -79,6 +95,13 @@ __device__ __forceinline__ half2_t scales_f16(uint32_t w) {
 }
 
 __device__ __forceinline__ half2_t bcast_lo(half2_t v) { return half2_t{v.x, v.x}; }
+
+// A wave-uniform value the compiler cannot see through (it is kept in an
+// SGPR and treated as produced at this point).
+__device__ __forceinline__ int32_t opaque_sgpr(int32_t v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
 __device__ __forceinline__ half2_t bcast_hi(half2_t v) { return half2_t{v.y, v.y}; }
 
 struct GemmParams {
@@ -104,19 +127,18 @@ struct GemmParams {
 
 }  // namespace
 
-template <int kWaves, int kMB, int kBK, bool kGated>
-__global__ __launch_bounds__(64 * kWaves, 2) void grouped_gemm_kernel(const GemmParams prm) {
+template <int kWaves, int kMB, int kBK, bool kGated, int kRing, int kOcc>
+__global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
+    const GemmParams prm) {
   constexpr int kThreads = 64 * kWaves;
   constexpr int kBM = 32 * kMB;
   constexpr int kLdA = kBK + 8;                          // fp16 per LDS row (16-byte pad)
-  constexpr int kChunks = kBM * (kBK / 32);              // 32-element A chunks per step
-  constexpr int kChunksPerThread = (kChunks + kThreads - 1) / kThreads;
   constexpr int kVec = kBK / 64;                         // 16-byte B loads per block per step
-  constexpr int kSteps = kBK / 16;                       // MFMAs (per block pair) per step
+  constexpr int kSteps = kBK / 16;                       // MFMA rounds per step
   __shared__ __align__(16) _Float16 smem[2 * kBM * kLdA];
   __shared__ int32_t s_off[kMaxExperts + 1];             // expert row offsets
   __shared__ int32_t s_mt[kMaxExperts + 1];              // m-tiles before each expert
-  __shared__ int32_t s_scan[8];
+  __shared__ int32_t s_scan[kWaves];
 
   // ---- once per workgroup: per-expert m-tile prefix in LDS -----------------
   {
@@ -157,6 +179,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void grouped_gemm_kernel(const Gemm
   const int32_t total_m = s_mt[prm.E];
   const int32_t total = total_m * prm.n_tiles;
   const int32_t per_xcd = (total + kXcds - 1) / kXcds;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5;
+  const int32_t K = prm.K;
+  const int64_t kb2 = K / 2, kb16 = K / 16;
+  const int nk = K / kBK;
 
   // ---- persistent loop over tiles; the workgroups on one XCD walk a
   // contiguous range of (m-tile, n-tile) so they share that XCD's L2 --------
@@ -177,10 +204,35 @@ __global__ __launch_bounds__(64 * kWaves, 2) void grouped_gemm_kernel(const Gemm
   const int32_t row0 = s_off[e] + (mt - s_mt[e]) * kBM;
   const int32_t rows = min(kBM, s_off[e + 1] - row0);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int32_t K = prm.K;
-  const int64_t kb2 = K / 2, kb16 = K / 16;
-  const int nk = K / kBK;
+  // ---- B streaming assignment: wave's 64 weight rows, 2 blocks of 32 ------
+  // GEMM1: block 0 = gate rows, block 1 = the matching up rows.  Weights are
+  // in the kernel layout (nvfp4_moe_pack_weights): inside each 32-row block,
+  // K step kt holds, lane by lane, the 16-byte pieces each lane consumes, so a
+  // wavefront's load is one contiguous 1 KB per piece (plus 64 contiguous
+  // scale groups of kBK/32 bytes).
+  const int32_t hc0 = kGated ? nt * (32 * kWaves) + 32 * wave : 0;   // h column base
+  const int32_t n0 = kGated ? 0 : nt * (64 * kWaves) + 64 * wave;    // output column base
+  const bool active = kGated ? hc0 < prm.I : n0 < prm.N_w;
+  const uint8_t* b_cp[2];
+  const uint8_t* b_sp[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    int32_t blk_row0;                                  // first row of the 32-row block
+    if (kGated) blk_row0 = j == 0 ? hc0 : prm.I + hc0;
+    else blk_row0 = n0 + 32 * j;
+    if (!active) blk_row0 = 0;                         // inactive waves read block 0
+    const int64_t rbase = (int64_t)e * prm.N_w + blk_row0;
+    b_cp[j] = prm.w_codes + rbase * kb2 + 16 * lane;
+    b_sp[j] = prm.w_sf + rbase * kb16 + (kBK / 32) * lane;
+  }
+
+  // The tile body, for kMBa = the number of 32-row sub-tiles that hold rows
+  // (the last tile of an expert may be partly empty: its empty sub-tiles
+  // are neither staged nor multiplied).
+  auto tile = [&](auto mbc) {
+  constexpr int kMBa = decltype(mbc)::value;
+  constexpr int kChunks = 32 * kMBa * (kBK / 32);       // 32-element A chunks per step
+  constexpr int kChunksPerThread = (kChunks + kThreads - 1) / kThreads;
 
   // ---- A staging assignment: chunk c -> (row, 32-wide k chunk) --------------
   const uint8_t* a_cp[kChunksPerThread];
@@ -199,38 +251,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void grouped_gemm_kernel(const Gemm
     a_lds[i] = r * kLdA + 32 * kc;
   }
 
-  // ---- B streaming assignment: wave's 64 weight rows, 2 blocks of 32 ------
-  // GEMM1: block 0 = gate rows, block 1 = the matching up rows.  Weights are
-  // in the kernel layout (nvfp4_moe_pack_weights): inside each 32-row block,
-  // K step kt holds, lane by lane, the 16-byte pieces each lane consumes, so a
-  // wavefront's load is one contiguous 1 KB per piece (plus 64 contiguous
-  // scale groups of kBK/32 bytes).
-  const int32_t hc0 = kGated ? nt * (32 * kWaves) + 32 * wave : 0;   // h column base
-  const int32_t n0 = kGated ? 0 : nt * (64 * kWaves) + 64 * wave;    // output column base
-  const bool active = kGated ? hc0 < prm.I : n0 < prm.N_w;
-  const int g = lane >> 5;
-  const uint8_t* b_cp[2];
-  const uint8_t* b_sp[2];
+  f32x16_t acc[kMBa][2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    int32_t blk_row0;                                  // first row of the 32-row block
-    if (kGated) blk_row0 = j == 0 ? hc0 : prm.I + hc0;
-    else blk_row0 = n0 + 32 * j;
-    if (!active) blk_row0 = 0;                         // inactive waves read block 0
-    const int64_t rbase = (int64_t)e * prm.N_w + blk_row0;
-    b_cp[j] = prm.w_codes + rbase * kb2 + 16 * lane;
-    b_sp[j] = prm.w_sf + rbase * kb16 + (kBK / 32) * lane;
-  }
-
-  f32x16_t acc[kMB][2];
-#pragma unroll
-  for (int i = 0; i < kMB; ++i)
+  for (int i = 0; i < kMBa; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
 
-  // Register rings (3 slots) for the packed codes of A and B: step kt's
-  // loads are issued two steps before their use.
-  constexpr int kRing = 3;
+  // Register rings (kRing slots) for the packed codes of A and B: step kt's
+  // loads are issued kRing - 1 steps before their use.
   u32x4 a_raw[kRing][kChunksPerThread];
   uint32_t a_sraw[kRing][kChunksPerThread];
   u32x4 b_raw[kRing][2][kVec];    // [slot][block][16-byte piece]
@@ -274,7 +302,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void grouped_gemm_kernel(const Gemm
       else b_sraw[buf][j] = *reinterpret_cast<const uint16_t*>(sp);
     }
   };
-  // One K step: kSteps MFMA rounds of (kMB x 2) 32x32x16 products on LDS
+  // One K step: kSteps MFMA rounds of (kMBa x 2) 32x32x16 products on LDS
   // buffer `lbuf` and B ring slot `buf`.  The operands of round s+1 (B
   // dequantised from registers, A read from LDS) are produced while round
   // s's MFMAs run.
@@ -297,22 +325,37 @@ __global__ __launch_bounds__(64 * kWaves, 2) void grouped_gemm_kernel(const Gemm
     auto aread = [&](int st, int i) -> half8_t {
       return *reinterpret_cast<const half8_t*>(abase + i * 32 * kLdA + 8 * st);
     };
-    half8_t bf[2], af[kMB];
+#if GEMM_SIMPLE_ROUNDS
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      half8_t bf[2], af[kMBa];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bf[j] = bdeq(st, j);
+#pragma unroll
+      for (int i = 0; i < kMBa; ++i) af[i] = aread(st, i);
+#pragma unroll
+      for (int i = 0; i < kMBa; ++i) {
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[0], acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[1], acc[i][1], 0, 0, 0);
+      }
+    }
+#else
+    half8_t bf[2], af[kMBa];
 #pragma unroll
     for (int j = 0; j < 2; ++j) bf[j] = bdeq(0, j);
 #pragma unroll
-    for (int i = 0; i < kMB; ++i) af[i] = aread(0, i);
+    for (int i = 0; i < kMBa; ++i) af[i] = aread(0, i);
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
-      half8_t nbf[2], naf[kMB];
+      half8_t nbf[2], naf[kMBa];
       if (st + 1 < kSteps) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) nbf[j] = bdeq(st + 1, j);
 #pragma unroll
-        for (int i = 0; i < kMB; ++i) naf[i] = aread(st + 1, i);
+        for (int i = 0; i < kMBa; ++i) naf[i] = aread(st + 1, i);
       }
 #pragma unroll
-      for (int i = 0; i < kMB; ++i) {
+      for (int i = 0; i < kMBa; ++i) {
         acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[0], acc[i][0], 0, 0, 0);
         acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[1], acc[i][1], 0, 0, 0);
       }
@@ -320,47 +363,51 @@ __global__ __launch_bounds__(64 * kWaves, 2) void grouped_gemm_kernel(const Gemm
 #pragma unroll
         for (int j = 0; j < 2; ++j) bf[j] = nbf[j];
 #pragma unroll
-        for (int i = 0; i < kMB; ++i) af[i] = naf[i];
+        for (int i = 0; i < kMBa; ++i) af[i] = naf[i];
       }
+#if GEMM_ROUND_BARRIER
+      __builtin_amdgcn_sched_barrier(0);
+#endif
     }
+#endif
   };
 
-  // ---- pipeline.  Ring slot of step x is x % 3; LDS buffer is x & 1.
-  // Step kt: issue A(kt+3) into the slot A(kt) left; in one basic block
+  // ---- pipeline.  Ring slot of step x is x % kRing; LDS buffer is x & 1.
+  // Step kt: issue A(kt+kRing) into the slot A(kt) left; in one basic block
   // dequantise A(kt+1) into LDS buffer (kt+1)&1 and run the MFMAs of step kt
-  // (LDS buffer kt&1, B slot kt%3) so the scheduler interleaves them; issue
-  // B(kt+3) into the slot just consumed; one barrier.  Whole groups of three
-  // steps loop with no early exit (so accumulators stay in place); the last
-  // one or two steps follow.
+  // (LDS buffer kt&1, B slot kt%kRing) so the scheduler interleaves them;
+  // issue B(kt+kRing) into the slot just consumed; one barrier.  Whole groups
+  // of kRing steps loop with no early exit (so accumulators stay in place);
+  // the remaining steps follow.
   load_a(0, Int<0>{});
   if (nk > 1) load_a(1, Int<1>{});
-  if (nk > 2) load_a(2, Int<2>{});
+  if constexpr (kRing > 2) if (nk > 2) load_a(2, Int<2 % kRing>{});
   load_b(0, Int<0>{});
   if (nk > 1) load_b(1, Int<1>{});
-  if (nk > 2) load_b(2, Int<2>{});
+  if constexpr (kRing > 2) if (nk > 2) load_b(2, Int<2 % kRing>{});
   store_a(0, Int<0>{});
   __syncthreads();
   auto step = [&](int kt, auto rc) {
     constexpr int r = decltype(rc)::value;
     constexpr int rn = (r + 1) % kRing;
-    if (kt + 3 < nk) load_a(kt + 3, Int<r>{});
+    if (kt + kRing < nk) load_a(kt + kRing, Int<r>{});
     if (active) {
       store_a((kt + 1) & 1, Int<rn>{});
       compute(kt & 1, Int<r>{});
     } else {
       store_a((kt + 1) & 1, Int<rn>{});
     }
-    if (kt + 3 < nk) load_b(kt + 3, Int<r>{});
+    if (kt + kRing < nk) load_b(kt + kRing, Int<r>{});
     __syncthreads();
   };
-  const int nk3 = nk - nk % 3;
-  for (int kt = 0; kt < nk3; kt += 3) {
+  const int nkr = nk - nk % kRing;
+  for (int kt = 0; kt < nkr; kt += kRing) {
     step(kt, Int<0>{});
-    step(kt + 1, Int<1>{});
-    step(kt + 2, Int<2>{});
+    step(kt + 1, Int<1 % kRing>{});
+    if constexpr (kRing > 2) step(kt + 2, Int<2 % kRing>{});
   }
-  if (nk3 < nk) step(nk3, Int<0>{});
-  if (nk3 + 1 < nk) step(nk3 + 1, Int<1>{});
+  if (nkr < nk) step(nkr, Int<0>{});
+  if constexpr (kRing > 2) if (nkr + 1 < nk) step(nkr + 1, Int<1>{});
 
   const float alpha = prm.in_scale[e] * prm.w_scale2[e];
   // MFMA 32x32 output layout: lane holds column (lane & 31) and rows
@@ -368,20 +415,54 @@ __global__ __launch_bounds__(64 * kWaves, 2) void grouped_gemm_kernel(const Gemm
   const int ccol = lane & 31, crow = 4 * g;
 
   if constexpr (!kGated) {
-    if (active)
+    // Each wavefront stages one 32 x 64 fp32 sub-tile at a time in its own
+    // LDS slice (rows padded to 72 floats: the two lane halves, 4 rows
+    // apart, land on disjoint banks), then writes whole 256-byte row
+    // segments with 16-byte stores.
+    constexpr int kLdc = 72;
+    constexpr bool kStaged = 2 * kBM * kLdA * 2 >= kWaves * 32 * kLdc * 4;
+    if constexpr (kStaged) {
+      float* sc = reinterpret_cast<float*>(smem) + wave * (32 * kLdc);
+      const int rr = lane >> 4, c4 = 4 * (lane & 15);
+      // row0 and ldc pass through an empty asm here so that the output
+      // addresses are formed after the K loop instead of being hoisted above
+      // it (where they would stay live across the loop).
+      const int32_t ldc = opaque_sgpr(prm.ldc);
+      const int32_t r0 = opaque_sgpr(row0);
+      float* gout = prm.c_out + (int64_t)r0 * ldc + n0 + c4;
+      if (active)
 #pragma unroll
-    for (int mi = 0; mi < kMB; ++mi)
+      for (int mi = 0; mi < kMBa; ++mi) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = mi * 32 + 8 * (i >> 2) + crow + (i & 3);
-          if (row < rows)
-            prm.c_out[(int64_t)(row0 + row) * prm.ldc + n0 + 32 * j + ccol] = alpha * acc[mi][j][i];
+          for (int i = 0; i < 16; ++i)
+            sc[(8 * (i >> 2) + crow + (i & 3)) * kLdc + 32 * j + ccol] = alpha * acc[mi][j][i];
+        // not unrolled: each row address is formed just before its store
+#pragma unroll 1
+        for (int q = 0; q < 8; ++q) {
+          const int r = 4 * q + rr;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(sc + r * kLdc + c4);
+          if (mi * 32 + r < rows)
+            *reinterpret_cast<f32x4*>(gout + (mi * 32 + r) * ldc) = v;
         }
+      }
+    } else {
+      if (active)
+#pragma unroll
+      for (int mi = 0; mi < kMBa; ++mi)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int row = mi * 32 + 8 * (i >> 2) + crow + (i & 3);
+            if (row < rows)
+              prm.c_out[(int64_t)(row0 + row) * prm.ldc + n0 + 32 * j + ccol] = alpha * acc[mi][j][i];
+          }
+    }
   } else {
-    // SiLU(gate) * up -> bf16 tile [BM][32 * kWaves] in LDS (the stage buffers
-    // are free: the loop's last barrier ordered all reads of them)
+    // SiLU(gate) * up -> bf16 tile [32 kMBa][32 * kWaves] in LDS (the stage
+    // buffers are free: the loop's last barrier ordered all reads of them)
     constexpr int kHW = 32 * kWaves;
     constexpr int kLdh = kHW + 8;
     static_assert(kLdh <= 2 * kLdA, "h tile must fit the stage buffers");
@@ -390,14 +471,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void grouped_gemm_kernel(const Gemm
     const int32_t I = prm.I;
     if (active) {
 #pragma unroll
-      for (int mi = 0; mi < kMB; ++mi)
+      for (int mi = 0; mi < kMBa; ++mi)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int row = mi * 32 + 8 * (i >> 2) + crow + (i & 3);
           const int col = 32 * wave + ccol;
           const float gv = alpha * acc[mi][0][i];
           const float uv = alpha * acc[mi][1][i];
-          const float hv = gv / (1.0f + __expf(-gv)) * uv;
+          // silu(g) = g / (1 + e^-g); the hardware reciprocal (1 ulp) is far
+          // inside the bf16 rounding that follows
+          const float hv = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
           const uint32_t hb = f32_to_bf16(hv);
           sh[row * kLdh + col] = (uint16_t)hb;
           if (row < rows) {
@@ -411,8 +494,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void grouped_gemm_kernel(const Gemm
         }
     }
     __syncthreads();
-    // requantise: BM rows x (kHW / 16) blocks of 16 columns
-    constexpr int kItems = kBM * (kHW / 16);
+    // requantise: rows x (kHW / 16) blocks of 16 columns
+    constexpr int kItems = 32 * kMBa * (kHW / 16);
     const float gs = prm.out_gscale[e];
     const int64_t ob2 = I / 2, ob16 = I / 16;
     for (int item = tid; item < kItems; item += kThreads) {
@@ -433,6 +516,20 @@ __global__ __launch_bounds__(64 * kWaves, 2) void grouped_gemm_kernel(const Gemm
       }
     }
   }
+  };  // tile
+
+  const int sub = (rows + 31) >> 5;                  // 32-row sub-tiles holding rows
+  if constexpr (kMB == 4) {
+    if (sub == 4) tile(Int<4>{});
+    else if (sub == 3) tile(Int<3>{});
+    else if (sub == 2) tile(Int<2>{});
+    else tile(Int<1>{});
+  } else if constexpr (kMB == 2) {
+    if (sub == 2) tile(Int<2>{});
+    else tile(Int<1>{});
+  } else {
+    tile(Int<kMB>{});
+  }
   __syncthreads();   // LDS is reused by the next tile
   }
 }
@@ -449,7 +546,7 @@ struct Residency {
   int cus = 0, per_cu = 0;
 };
 
-template <int kWaves, int kMB, int kBK, bool kGated>
+template <int kWaves, int kMB, int kBK, bool kGated, int kRing, int kOcc>
 hipError_t launch(GemmParams prm, int32_t P, hipStream_t stream) {
   constexpr int kBM = 32 * kMB;
   static Residency res;
@@ -459,7 +556,7 @@ hipError_t launch(GemmParams prm, int32_t P, hipStream_t stream) {
     if (err == hipSuccess) err = hipDeviceGetAttribute(&res.cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (err == hipSuccess)
       err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &res.per_cu, (const void*)grouped_gemm_kernel<kWaves, kMB, kBK, kGated>, 64 * kWaves, 0);
+          &res.per_cu, (const void*)grouped_gemm_kernel<kWaves, kMB, kBK, kGated, kRing, kOcc>, 64 * kWaves, 0);
     if (err != hipSuccess) return err;
     if (res.per_cu < 1) res.per_cu = 1;
   }
@@ -467,15 +564,16 @@ hipError_t launch(GemmParams prm, int32_t P, hipStream_t stream) {
   const int64_t slots = (int64_t)res.cus * res.per_cu;
   int64_t grid = tiles < slots ? tiles : slots;
   grid = (grid + kXcds - 1) / kXcds * kXcds;            // whole XCD rounds
-  hipLaunchKernelGGL((grouped_gemm_kernel<kWaves, kMB, kBK, kGated>), dim3((uint32_t)grid),
+  hipLaunchKernelGGL((grouped_gemm_kernel<kWaves, kMB, kBK, kGated, kRing, kOcc>), dim3((uint32_t)grid),
                      dim3(64 * kWaves), 0, stream, prm);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Tile height: 64 token rows when experts average at least 32 rows (prefill),
-// else 32 (decode-like batches, weight-streaming bound).
+// Tile height: 128 token rows when experts average at least 32 rows (prefill;
+// the last tile of an expert runs only its occupied 32-row sub-tiles), else
+// 32 (decode-like batches, weight-streaming bound).
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream) {
   if (a.P == 0) return hipSuccess;
   GemmParams prm{};
@@ -486,8 +584,8 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream) {
   prm.c1_dbg = a.c1_dbg; prm.h_dbg = a.h_dbg;
   constexpr int kWaves = 4;
   prm.n_tiles = (a.I + 32 * kWaves - 1) / (32 * kWaves);
-  if (a.P >= 32 * a.E) return launch<kWaves, 2, 128, true>(prm, a.P, stream);
-  return launch<kWaves, 1, 128, true>(prm, a.P, stream);
+  if (a.P >= 32 * a.E) return launch<kWaves, G1_MB, G1_BK, true, G1_RING, G1_OCC>(prm, a.P, stream);
+  return launch<kWaves, 1, G1_BK, true, 3, 2>(prm, a.P, stream);
 }
 
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream) {
@@ -499,8 +597,8 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream) {
   prm.c_out = a.out; prm.ldc = a.H;
   constexpr int kWaves = 4;
   prm.n_tiles = (a.H + 64 * kWaves - 1) / (64 * kWaves);
-  if (a.P >= 32 * a.E) return launch<kWaves, 2, 64, false>(prm, a.P, stream);
-  return launch<kWaves, 1, 64, false>(prm, a.P, stream);
+  if (a.P >= 32 * a.E) return launch<kWaves, G2_MB, 64, false, G2_RING, G2_OCC>(prm, a.P, stream);
+  return launch<kWaves, 1, 64, false, 3, 2>(prm, a.P, stream);
 }
 
 // ---- load-time weight layout conversion -----------------------------------
@@ -547,7 +645,7 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restr
   for (int32_t i = 0; i < per; ++i) dst[gi * per + i] = src[row * (K / 16) + blk + i];
 }
 
-int32_t weight_step_k(int32_t projection) { return projection == 0 ? 128 : 64; }
+int32_t weight_step_k(int32_t projection) { return projection == 0 ? G1_BK : 64; }
 
 hipError_t launch_pack_weights(int32_t projection, const uint8_t* codes, const uint8_t* sf,
                                int32_t E, int32_t N, int32_t K, uint8_t* codes_out,
