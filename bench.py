@@ -42,7 +42,20 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=64)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (the "
+                         "known-size reference for the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def copy_calibration(torch):
+    n = 1 << 28                                   # 2^28 fp32 = 1 GiB
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log("copy calibration: 3 x 1 GiB device copy done")
 
 
 class HipEvents:
@@ -85,6 +98,32 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemm1_w13_prefill_pmc.md")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the w13 GEMM from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE record, or None when the kernel sources have
+    changed since those counters were taken."""
+    import hashlib
+    try:
+        rec = {}
+        for line in open(TRAFFIC_RECORD):
+            key, sep, val = line.partition(":")
+            if sep and key.strip() and " " not in key.strip():
+                rec[key.strip()] = val.strip()
+        h = hashlib.sha256()
+        for f in rec["sources"].split():
+            with open(os.path.join(ROOT, f), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest() != rec["sources_sha256"]:
+            return None
+        return int(rec["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def build_layer(w, torch, M):
     """Seeded bf16 expert weights -> NVFP4 with the library's quantiser;
     activation scales calibrated with the library's kernels."""
@@ -125,6 +164,12 @@ def bench_layer(args, torch, M, L, events):
         x, lg, out = sets[i % 3]
         L.moe_forward(wstruct, x, lg, w.T, w.k, None, out, ws, nbytes, dbg, stream)
 
+    # Every timed step also records HIP events between its launches (on the
+    # library's stream), so the per-kernel times come from the timed region.
+    nst = len(L.MOE_STAGES)
+    evs = [events.create(nst + 1) for _ in range(args.steps)]
+    dbgs = [L.MoEDebug(stage_events=ctypes.cast(e, ctypes.POINTER(ctypes.c_void_p))) for e in evs]
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -132,7 +177,7 @@ def bench_layer(args, torch, M, L, events):
     events.record(ev[0], stream)
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        step(i, dbgs[i])
     events.record(ev[1], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -140,20 +185,12 @@ def bench_layer(args, torch, M, L, events):
     events.destroy(ev)
     ms_step = ms_total / args.steps
 
-    # per-stage times: the same steps with events between the launches
-    nst = len(L.MOE_STAGES)
-    n2 = min(args.steps, 50)
-    evs = [events.create(nst + 1) for _ in range(n2)]
-    dbgs = [L.MoEDebug(stage_events=ctypes.cast(e, ctypes.POINTER(ctypes.c_void_p))) for e in evs]
-    for i in range(n2):
-        step(i, dbgs[i])
-    torch.cuda.synchronize()
     stage_ms = np.zeros(nst)
     for e in evs:
         for s in range(nst):
             stage_ms[s] += events.elapsed_ms(e[s], e[s + 1])
         events.destroy(e)
-    stage_us = {name: 1000.0 * v / n2 for name, v in zip(L.MOE_STAGES, stage_ms)}
+    stage_us = {name: 1000.0 * v / args.steps for name, v in zip(L.MOE_STAGES, stage_ms)}
     return w, layer, ms_step, wall, stage_us
 
 
@@ -260,6 +297,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     from nvfp4_w4a4_expert_amd import _lib as L
     from nvfp4_w4a4_expert_amd import moe as M
     events = HipEvents()
@@ -276,7 +316,8 @@ def main():
         ach = flops_gemm1 / (g1 * 1e-6) / 1e12
         roofline = dict(kernel="grouped_gemm_kernel<true> (w13 + SiLU*mul + requant)",
                         bound="mfma", achieved=round(ach, 1), peak=MFMA_F16_PEAK_TFLOPS,
-                        unit="TFLOP/s", frac=round(ach / MFMA_F16_PEAK_TFLOPS, 4), traffic=None,
+                        unit="TFLOP/s", frac=round(ach / MFMA_F16_PEAK_TFLOPS, 4),
+                        traffic=measured_traffic(),
                         algorithmic_flops=flops_gemm1, us_per_launch=round(g1, 2))
     else:
         # weight streaming: algorithmic bytes = NVFP4 w13 of every expert hit

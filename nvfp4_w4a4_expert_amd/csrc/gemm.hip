@@ -16,14 +16,17 @@
 //
 // Work split.  A workgroup owns BM token rows of one expert (BM = 32 * kMB)
 // and 64 * kWaves weight rows; wavefront w owns weight rows [64w, 64w + 64)
-// of the tile and all BM token rows.
+// of the tile and all BM token rows.  The last tile of an expert runs only
+// its occupied 32-row sub-tiles (a separate instantiation of the tile body),
+// so padding costs at most 31 rows per expert.
 //  * The token operand A is shared by every wavefront: each K step it is
 //    loaded once per workgroup, dequantised to fp16 and staged in LDS
 //    (double buffered, rows padded by 16 bytes so the 16-byte fragment reads
 //    of 16 consecutive lanes hit distinct banks).
 //  * The weight operand B is private to its wavefront: each lane streams its
-//    row's packed codes straight from global memory into registers two K
-//    steps ahead and dequantises 8 values per MFMA just before use (the
+//    row's packed codes straight from global memory into a register ring
+//    (kRing slots, loads kRing - 1 K steps ahead) and dequantises 8 values
+//    per MFMA just before use (the
 //    gfx950 FP4 -> fp16 pair conversion, then one packed fp16 multiply by the
 //    block scale).  Weights never pass through LDS.
 //  * K order inside a step is permuted identically for A and B so that each
@@ -43,7 +46,8 @@
 //
 // GEMM1 pairs columns: wavefront w's 64 weight rows are 32 gate rows and the
 // 32 matching up rows, so SiLU*mul happens in registers and the tile's h
-// columns are requantised from LDS in blocks of 16.
+// columns are requantised from LDS in blocks of 16.  GEMM2 stages each
+// 32 x 64 fp32 sub-tile in LDS and writes whole rows with 16-byte stores.
 #include <type_traits>
 
 #include "internal.h"
@@ -58,21 +62,14 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kXcds = 8;
 
-#ifndef GEMM_SIMPLE_ROUNDS
-#define GEMM_SIMPLE_ROUNDS 0
-#endif
-#ifndef GEMM_ROUND_BARRIER
-#define GEMM_ROUND_BARRIER 0
-#endif
-#ifndef G1_MB
-#define G1_MB 2
-#define G1_BK 128
-#define G1_RING 3
-#define G1_OCC 2
-#define G2_MB 4
-#define G2_RING 2
-#define G2_OCC 2
-#endif
+// Launch shapes for batches with at least 32 rows per expert on average
+// (chosen by measurement on MI355X at the 4096-token prefill layer):
+//   w13: 64-row tiles, K step 128, 3-slot register rings, 2 workgroups/CU
+//   w2:  128-row tiles, K step 64, 2-slot register rings, 2 workgroups/CU
+// (256 VGPRs per lane either way; a 128-row w13 tile with 3-slot rings does
+// not fit and with 2-slot rings loses more to latency than it gains.)
+constexpr int kG1MB = 2, kG1BK = 128, kG1Ring = 3, kG1Occ = 2;
+constexpr int kG2MB = 4, kG2Ring = 2, kG2Occ = 2;
 constexpr int kMaxExperts = 1024;
 
 template <int V>
@@ -325,21 +322,6 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
     auto aread = [&](int st, int i) -> half8_t {
       return *reinterpret_cast<const half8_t*>(abase + i * 32 * kLdA + 8 * st);
     };
-#if GEMM_SIMPLE_ROUNDS
-#pragma unroll
-    for (int st = 0; st < kSteps; ++st) {
-      half8_t bf[2], af[kMBa];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = bdeq(st, j);
-#pragma unroll
-      for (int i = 0; i < kMBa; ++i) af[i] = aread(st, i);
-#pragma unroll
-      for (int i = 0; i < kMBa; ++i) {
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[0], acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[1], acc[i][1], 0, 0, 0);
-      }
-    }
-#else
     half8_t bf[2], af[kMBa];
 #pragma unroll
     for (int j = 0; j < 2; ++j) bf[j] = bdeq(0, j);
@@ -365,11 +347,7 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
 #pragma unroll
         for (int i = 0; i < kMBa; ++i) af[i] = naf[i];
       }
-#if GEMM_ROUND_BARRIER
-      __builtin_amdgcn_sched_barrier(0);
-#endif
     }
-#endif
   };
 
   // ---- pipeline.  Ring slot of step x is x % kRing; LDS buffer is x & 1.
@@ -584,8 +562,8 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream) {
   prm.c1_dbg = a.c1_dbg; prm.h_dbg = a.h_dbg;
   constexpr int kWaves = 4;
   prm.n_tiles = (a.I + 32 * kWaves - 1) / (32 * kWaves);
-  if (a.P >= 32 * a.E) return launch<kWaves, G1_MB, G1_BK, true, G1_RING, G1_OCC>(prm, a.P, stream);
-  return launch<kWaves, 1, G1_BK, true, 3, 2>(prm, a.P, stream);
+  if (a.P >= 32 * a.E) return launch<kWaves, kG1MB, kG1BK, true, kG1Ring, kG1Occ>(prm, a.P, stream);
+  return launch<kWaves, 1, kG1BK, true, 3, 2>(prm, a.P, stream);
 }
 
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream) {
@@ -597,7 +575,7 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream) {
   prm.c_out = a.out; prm.ldc = a.H;
   constexpr int kWaves = 4;
   prm.n_tiles = (a.H + 64 * kWaves - 1) / (64 * kWaves);
-  if (a.P >= 32 * a.E) return launch<kWaves, G2_MB, 64, false, G2_RING, G2_OCC>(prm, a.P, stream);
+  if (a.P >= 32 * a.E) return launch<kWaves, kG2MB, 64, false, kG2Ring, kG2Occ>(prm, a.P, stream);
   return launch<kWaves, 1, 64, false, 3, 2>(prm, a.P, stream);
 }
 
@@ -645,7 +623,7 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restr
   for (int32_t i = 0; i < per; ++i) dst[gi * per + i] = src[row * (K / 16) + blk + i];
 }
 
-int32_t weight_step_k(int32_t projection) { return projection == 0 ? G1_BK : 64; }
+int32_t weight_step_k(int32_t projection) { return projection == 0 ? kG1BK : 64; }
 
 hipError_t launch_pack_weights(int32_t projection, const uint8_t* codes, const uint8_t* sf,
                                int32_t E, int32_t N, int32_t K, uint8_t* codes_out,
