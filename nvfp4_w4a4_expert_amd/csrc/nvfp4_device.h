@@ -39,21 +39,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 
 // Non-negative fp32 (or +inf) -> E4M3 code 0x00..0x7E: nearest finite value,
 // ties to the even code, saturating at 448 (0x7E; 0x7F is NaN in E4M3).
+// Branch-free: both the subnormal and the normal candidate are formed and one
+// is selected.
 __device__ __forceinline__ uint32_t e4m3_encode(float s) {
-  if (!(s < kE4M3Max)) return 0x7Eu;
-  const uint32_t u = __float_as_uint(s);
-  const int e = (int)(u >> 23) - 127;              // exponent of s (-127 for 0 / fp32 denormals)
-  if (e < -6) {
-    // E4M3 subnormal range: multiples of 2^-9 (code == multiple, 8 == 2^-6).
-    // s * 512 is exact (power-of-two scaling of a value far from overflow);
-    // rintf rounds to nearest even.
-    return (uint32_t)__builtin_rintf(s * 512.0f);
-  }
+  // NaN, +inf and everything >= 448 saturate: fminf returns 448 for them
+  const float c = fminf(s, kE4M3Max);
+  const uint32_t u = __float_as_uint(c);
+  const int e = (int)(u >> 23) - 127;              // exponent of c (-127 for 0 / fp32 denormals)
+  // E4M3 subnormal range (c < 2^-6): multiples of 2^-9 (code == multiple,
+  // 8 == 2^-6).  c * 512 is exact; rintf rounds to nearest even.
+  const uint32_t sub = (uint32_t)__builtin_rintf(c * 512.0f);
   const uint32_t mant = u & 0x7FFFFFu;
   uint32_t code = ((uint32_t)(e + 7) << 3) | (mant >> 20);
   const uint32_t rem = mant & 0xFFFFFu;               // dropped 20 mantissa bits
   code += (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) ? 1u : 0u;
-  return code;                                       // s < 448 keeps this <= 0x7E
+  return e < -6 ? sub : code;                        // c <= 448 keeps code <= 0x7E
 }
 
 // E4M3 code (non-negative, finite) -> fp32 value, exact and branch-free.

@@ -1,11 +1,12 @@
 // Per-expert NVFP4 activation quantiser for gfx950 (page 3, "NVFP4" section,
 // runtime-order figure; SFScale[expert_idx] excerpt).
 //
-// Token-major: one thread owns one 16-element block of one source row.  It
-// loads the 32 bytes once, forms amax/6 once, and then, for each of the row's
-// topk destinations, applies that expert's SFScaleVal, encodes the 16 codes
-// and stores 8 bytes of packed codes plus one E4M3 byte.  Consecutive threads
-// own consecutive blocks, so loads and stores of a wavefront are contiguous.
+// Token-major: a workgroup owns one source row, one 16-element block per
+// lane.  The row, its topk destinations and their SFScaleVals are uniform
+// (scalar loads); each lane loads its block once,
+// forms amax/6 once, and for every destination applies that expert's
+// SFScaleVal, encodes 16 codes and stores 8 bytes of packed codes plus one
+// E4M3 byte.  A wavefront's loads and stores are contiguous.
 // The kernel is HBM-bound: it reads each source row once and writes
 // topk * (K/2 + K/16) bytes per row.
 #include "internal.h"
@@ -13,38 +14,66 @@
 
 namespace nvfp4 {
 
-__global__ __launch_bounds__(256) void quantize_experts_kernel(
+// kE / kP / kG: expert_idx / dst_row / gscale are present (not null).
+template <bool kE, bool kP, bool kG>
+__global__ __launch_bounds__(1024) void quantize_experts_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int32_t num_rows, int32_t nblk, int32_t topk,
     const int32_t* __restrict__ expert_idx, const int32_t* __restrict__ dst_row,
     int32_t num_experts, const float* __restrict__ gscale, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ sf, int32_t num_dst_rows) {
 #pragma clang fp contract(off)
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= (int64_t)num_rows * nblk) return;
-  const int32_t t = (int32_t)(g / nblk);
-  const int32_t b = (int32_t)(g - (int64_t)t * nblk);
+  // One workgroup per source row (wave-uniform t); thread -> block b.  The
+  // whole row, and so every destination row's codes and scale bytes, is
+  // written from one CU and one L2.
+  const int32_t t = (int32_t)blockIdx.x;
+  const int32_t b = (int32_t)blockIdx.y * (int32_t)blockDim.x + (int32_t)threadIdx.x;
+  const bool on = b < nblk;
 
-  const u32x4* src = reinterpret_cast<const u32x4*>(x + (int64_t)t * ldx + (int64_t)b * 16);
-  const u32x4 v0 = __builtin_nontemporal_load(src);
-  const u32x4 v1 = __builtin_nontemporal_load(src + 1);
   float xv[16];
-  unpack_bf16x8(v0, xv);
-  unpack_bf16x8(v1, xv + 8);
-  const float a6 = absmax16(xv) / kE2M1Max;
+  float a6 = 0.0f;
+  if (on) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + (int64_t)t * ldx + (int64_t)b * 16);
+    const u32x4 v0 = __builtin_nontemporal_load(src);
+    const u32x4 v1 = __builtin_nontemporal_load(src + 1);
+    unpack_bf16x8(v0, xv);
+    unpack_bf16x8(v1, xv + 8);
+    a6 = absmax16(xv) / kE2M1Max;
+  }
 
   const int64_t row_bytes = (int64_t)nblk * 8;
-  for (int32_t j = 0; j < topk; ++j) {
-    const int64_t q = (int64_t)t * topk + j;
-    const int32_t e = expert_idx ? expert_idx[q] : 0;
-    const int32_t p = dst_row ? dst_row[q] : (int32_t)q;
-    if ((uint32_t)p >= (uint32_t)num_dst_rows || (uint32_t)e >= (uint32_t)num_experts) continue;
-    const float gs = gscale ? gscale[e] : 1.0f;
-    const BlockScale bs = block_scale(a6, gs);
-    uint2 w;
-    w.x = encode8(xv, bs.inv);
-    w.y = encode8(xv + 8, bs.inv);
-    *reinterpret_cast<uint2*>(codes + (int64_t)p * row_bytes + (int64_t)b * 8) = w;
-    sf[(int64_t)p * nblk + b] = (uint8_t)bs.sf;
+  // Destinations in batches of 8 (scalar loads shared by the wavefront): the
+  // batch's expert ids and rows, then their SFScaleVals, are fetched before
+  // any encoding, so the load latencies overlap.
+  constexpr int kBatch = 8;
+  for (int32_t j0 = 0; j0 < topk; j0 += kBatch) {
+    int32_t eb[kBatch], pb[kBatch];
+    float gb[kBatch];
+#pragma unroll
+    for (int jj = 0; jj < kBatch; ++jj) {
+      // slots past topk re-read the last slot (always in range) and are
+      // skipped below, so every load is unconditional
+      const int64_t q = (int64_t)t * topk + min(j0 + jj, topk - 1);
+      eb[jj] = kE ? expert_idx[q] : 0;
+      pb[jj] = kP ? dst_row[q] : (int32_t)q;
+    }
+#pragma unroll
+    for (int jj = 0; jj < kBatch; ++jj) {
+      const int32_t ec = min(max(eb[jj], 0), num_experts - 1);   // clamped for the load
+      gb[jj] = kG ? gscale[ec] : 1.0f;
+    }
+#pragma unroll
+    for (int jj = 0; jj < kBatch; ++jj) {
+      const int32_t e = eb[jj], p = pb[jj];
+      if (j0 + jj >= topk || (uint32_t)p >= (uint32_t)num_dst_rows ||
+          (uint32_t)e >= (uint32_t)num_experts || !on)
+        continue;
+      const BlockScale bs = block_scale(a6, gb[jj]);
+      uint2 w;
+      w.x = encode8(xv, bs.inv);
+      w.y = encode8(xv + 8, bs.inv);
+      *reinterpret_cast<uint2*>(codes + (int64_t)p * row_bytes + (int64_t)b * 8) = w;
+      sf[(int64_t)p * nblk + b] = (uint8_t)bs.sf;
+    }
   }
 }
 
@@ -53,12 +82,29 @@ hipError_t launch_quantize(const uint16_t* x, int64_t ldx, int32_t num_rows, int
                            int32_t num_experts, const float* gscale, uint8_t* codes, uint8_t* sf,
                            int32_t num_dst_rows, hipStream_t stream) {
   const int32_t nblk = K / 16;
-  const int64_t total = (int64_t)num_rows * nblk;
-  if (total == 0) return hipSuccess;
-  const int64_t grid = (total + 255) / 256;
-  hipLaunchKernelGGL(quantize_experts_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, x, ldx,
-                     num_rows, nblk, topk, expert_idx, dst_row, num_experts, gscale, codes, sf,
-                     num_dst_rows);
+  if ((int64_t)num_rows * nblk == 0) return hipSuccess;
+  // 64-lane wavefronts covering the row's blocks, at most 1024 threads per
+  // workgroup (longer rows take several workgroups)
+  const int32_t threads = min(1024, (nblk + 63) / 64 * 64);
+  const dim3 grid((uint32_t)num_rows, (uint32_t)((nblk + threads - 1) / threads));
+  const int variant = (expert_idx ? 4 : 0) | (dst_row ? 2 : 0) | (gscale ? 1 : 0);
+#define NVFP4_QUANT_CASE(v, ke, kp, kg)                                                         \
+  case v:                                                                                       \
+    hipLaunchKernelGGL((quantize_experts_kernel<ke, kp, kg>), grid, dim3(threads), 0, stream, x,    \
+                       ldx, num_rows, nblk, topk, expert_idx, dst_row, num_experts, gscale,     \
+                       codes, sf, num_dst_rows);                                                \
+    break;
+  switch (variant) {
+    NVFP4_QUANT_CASE(0, false, false, false)
+    NVFP4_QUANT_CASE(1, false, false, true)
+    NVFP4_QUANT_CASE(2, false, true, false)
+    NVFP4_QUANT_CASE(3, false, true, true)
+    NVFP4_QUANT_CASE(4, true, false, false)
+    NVFP4_QUANT_CASE(5, true, false, true)
+    NVFP4_QUANT_CASE(6, true, true, false)
+    NVFP4_QUANT_CASE(7, true, true, true)
+  }
+#undef NVFP4_QUANT_CASE
   return hipGetLastError();
 }
 

@@ -193,6 +193,16 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   const int32_t q0 = (int32_t)blockIdx.x * span;
   const int32_t q1 = min(P, q0 + span);
 
+  // the block's own ids (its first kOwn steps) are loaded first, so their
+  // latency overlaps the histogram
+  constexpr int kOwn = 4;
+  int32_t own[kOwn];
+#pragma unroll
+  for (int u = 0; u < kOwn; ++u) {
+    const int64_t q = (int64_t)q0 + u * kPermThreads + tid;
+    own[u] = q < q1 ? ids[q] : -1;
+  }
+
   for (int e = tid; e < E; e += kPermThreads) {
     s_before[e] = 0;
     s_after[e] = 0;
@@ -201,8 +211,9 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   }
   __syncthreads();
 
-  // 1. histogram of all pairs
-  constexpr int kUnroll = 8;
+  // 1. histogram of all pairs (all loads of a round are issued before its
+  // LDS additions)
+  constexpr int kUnroll = 32;
   for (int64_t qb = 0; qb < P; qb += kPermThreads * kUnroll) {
     int32_t id[kUnroll];
 #pragma unroll
@@ -240,10 +251,9 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 
   // 3. stable ranks inside the block
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int64_t qs = q0; qs < q1; qs += kPermThreads) {
+  auto rank_step = [&](int64_t qs, int32_t id) {
     const int32_t q = (int32_t)min(qs + tid, (int64_t)q1);
-    const int32_t id = q < q1 ? ids[q] : -1;
-    const bool valid = (uint32_t)id < (uint32_t)E;
+    const bool valid = q < q1 && (uint32_t)id < (uint32_t)E;
     uint64_t same = __ballot(valid);
     for (int b = 0; b < id_bits; ++b) {
       const bool bit = (id >> b) & 1;
@@ -273,6 +283,15 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     // barrier, and its LDS operations complete in program order, so the
     // leader clears its entry after every lane of the wavefront has read it.
     if (leader) s_wave[wave][id] = 0;
+  };
+#pragma unroll
+  for (int u = 0; u < kOwn; ++u) {
+    const int64_t qs = (int64_t)q0 + u * kPermThreads;
+    if (qs < q1) rank_step(qs, own[u]);        // uniform condition
+  }
+  for (int64_t qs = (int64_t)q0 + kOwn * kPermThreads; qs < q1; qs += kPermThreads) {
+    const int64_t q = qs + tid;
+    rank_step(qs, q < q1 ? ids[q] : -1);
   }
 }
 
