@@ -93,6 +93,16 @@ __device__ __forceinline__ half2_t scales_f16(uint32_t w) {
 
 __device__ __forceinline__ half2_t bcast_lo(half2_t v) { return half2_t{v.x, v.x}; }
 
+// Workgroup barrier that orders LDS accesses only.  Every barrier in these
+// kernels hands LDS data between threads; none publishes global memory, so
+// outstanding global loads (the register rings' prefetches) need not drain,
+// which a full __syncthreads() fence would make the compiler wait for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // A wave-uniform value the compiler cannot see through (it is kept in an
 // SGPR and treated as produced at this point).
 __device__ __forceinline__ int32_t opaque_sgpr(int32_t v) {
@@ -162,7 +172,7 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
       if (lane >= off) incl += o;
     }
     if (lane == 63) s_scan[wave] = incl;
-    __syncthreads();
+    lds_barrier();
     int32_t base = incl - total;
     for (int w = 0; w < wave; ++w) base += s_scan[w];
 #pragma unroll
@@ -171,7 +181,7 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
       if (e <= prm.E) s_mt[e] = base;
       base += cnt[i];
     }
-    __syncthreads();
+    lds_barrier();
   }
   const int32_t total_m = s_mt[prm.E];
   const int32_t total = total_m * prm.n_tiles;
@@ -239,7 +249,7 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
 #pragma unroll
   for (int i = 0; i < kChunksPerThread; ++i) {
     const int c = tid + i * kThreads;
-    a_on[i] = c < kChunks;
+    a_on[i] = kChunks % kThreads == 0 || c < kChunks;   // compile-time true when exact
     const int cc = a_on[i] ? c : 0;
     const int r = cc / (kBK / 32), kc = cc % (kBK / 32);
     const int64_t arow = row0 + min(r, rows - 1);
@@ -357,26 +367,33 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
   // issue B(kt+kRing) into the slot just consumed; one barrier.  Whole groups
   // of kRing steps loop with no early exit (so accumulators stay in place);
   // the remaining steps follow.
+  // prologue in the steady state's issue order (A then B of each step)
   load_a(0, Int<0>{});
-  if (nk > 1) load_a(1, Int<1>{});
-  if constexpr (kRing > 2) if (nk > 2) load_a(2, Int<2 % kRing>{});
   load_b(0, Int<0>{});
-  if (nk > 1) load_b(1, Int<1>{});
-  if constexpr (kRing > 2) if (nk > 2) load_b(2, Int<2 % kRing>{});
+  load_a(min(1, nk - 1), Int<1>{});
+  load_b(min(1, nk - 1), Int<1>{});
+  if constexpr (kRing > 2) {
+    load_a(min(2, nk - 1), Int<2 % kRing>{});
+    load_b(min(2, nk - 1), Int<2 % kRing>{});
+  }
   store_a(0, Int<0>{});
-  __syncthreads();
+  lds_barrier();
   auto step = [&](int kt, auto rc) {
     constexpr int r = decltype(rc)::value;
     constexpr int rn = (r + 1) % kRing;
-    if (kt + kRing < nk) load_a(kt + kRing, Int<r>{});
+    // Loads are issued unconditionally (steps past the end re-read the last
+    // step, which is harmless): a load under a branch makes the compiler's
+    // wait counting fall back to waiting for every outstanding load, which
+    // would defeat the ring.
+    load_a(min(kt + kRing, nk - 1), Int<r>{});
     if (active) {
       store_a((kt + 1) & 1, Int<rn>{});
       compute(kt & 1, Int<r>{});
     } else {
       store_a((kt + 1) & 1, Int<rn>{});
     }
-    if (kt + kRing < nk) load_b(kt + kRing, Int<r>{});
-    __syncthreads();
+    load_b(min(kt + kRing, nk - 1), Int<r>{});
+    lds_barrier();
   };
   const int nkr = nk - nk % kRing;
   for (int kt = 0; kt < nkr; kt += kRing) {
@@ -471,7 +488,7 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
           }
         }
     }
-    __syncthreads();
+    lds_barrier();
     // requantise: rows x (kHW / 16) blocks of 16 columns
     constexpr int kItems = 32 * kMBa * (kHW / 16);
     const float gs = prm.out_gscale[e];
@@ -497,18 +514,22 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
   };  // tile
 
   const int sub = (rows + 31) >> 5;                  // 32-row sub-tiles holding rows
-  if constexpr (kMB == 4) {
-    if (sub == 4) tile(Int<4>{});
-    else if (sub == 3) tile(Int<3>{});
-    else if (sub == 2) tile(Int<2>{});
-    else tile(Int<1>{});
-  } else if constexpr (kMB == 2) {
-    if (sub == 2) tile(Int<2>{});
-    else tile(Int<1>{});
-  } else {
+  static_assert(kMB >= 1 && kMB <= 4, "tile height is 32 to 128 rows");
+  if (sub >= kMB) {
     tile(Int<kMB>{});
+  } else {
+    if constexpr (kMB == 4) {
+      if (sub == 3) tile(Int<3>{});
+      else if (sub == 2) tile(Int<2>{});
+      else tile(Int<1>{});
+    } else if constexpr (kMB == 3) {
+      if (sub == 2) tile(Int<2>{});
+      else tile(Int<1>{});
+    } else if constexpr (kMB == 2) {
+      tile(Int<1>{});
+    }
   }
-  __syncthreads();   // LDS is reused by the next tile
+  lds_barrier();   // LDS is reused by the next tile
   }
 }
 
