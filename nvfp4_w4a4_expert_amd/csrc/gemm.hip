@@ -59,16 +59,21 @@ namespace {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kXcds = 8;
 
 // Launch shapes for batches with at least 32 rows per expert on average
 // (chosen by measurement on MI355X at the 4096-token prefill layer):
-//   w13: 64-row tiles, K step 128, 3-slot register rings, 2 workgroups/CU
-//   w2:  128-row tiles, K step 64, 2-slot register rings, 2 workgroups/CU
-// (256 VGPRs per lane either way; a 128-row w13 tile with 3-slot rings does
-// not fit and with 2-slot rings loses more to latency than it gains.)
-constexpr int kG1MB = 2, kG1BK = 128, kG1Ring = 3, kG1Occ = 2;
+//   w13: 8 wavefronts (256 h columns), 64-row tiles, K step 128, 3-slot
+//        register rings, one workgroup per CU: the staged token tile serves
+//        twice the weight columns of a 4-wavefront workgroup
+//   w2:  4 wavefronts (256 output columns), 128-row tiles, K step 64, 2-slot
+//        register rings, 2 workgroups per CU
+// (two wavefronts per SIMD, at most 256 VGPRs per lane; 96- or 128-row w13
+// tiles either do not fit with 3-slot rings or lose more to latency with
+// 2-slot rings than they save in dequantisation.)
+constexpr int kG1Waves = 8, kG1MB = 2, kG1BK = 128, kG1Ring = 3, kG1Occ = 1;
 constexpr int kG2MB = 4, kG2Ring = 2, kG2Occ = 2;
 constexpr int kMaxExperts = 1024;
 
@@ -238,10 +243,15 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
   // are neither staged nor multiplied).
   auto tile = [&](auto mbc) {
   constexpr int kMBa = decltype(mbc)::value;
-  constexpr int kChunks = 32 * kMBa * (kBK / 32);       // 32-element A chunks per step
+  // A is staged in chunks of 32 elements (16 code bytes + 2 scales), or of
+  // 16 elements when that is what it takes to give every thread a chunk.
+  constexpr int kCE = 32 * kMBa * (kBK / 32) >= kThreads ? 32 : 16;
+  constexpr int kCPR = kBK / kCE;                        // chunks per row per step
+  constexpr int kChunks = 32 * kMBa * kCPR;
   constexpr int kChunksPerThread = (kChunks + kThreads - 1) / kThreads;
+  using araw_t = std::conditional_t<kCE == 32, u32x4, u32x2>;
 
-  // ---- A staging assignment: chunk c -> (row, 32-wide k chunk) --------------
+  // ---- A staging assignment: chunk c -> (row, kCE-wide k chunk) -------------
   const uint8_t* a_cp[kChunksPerThread];
   const uint8_t* a_sp[kChunksPerThread];
   int a_lds[kChunksPerThread];
@@ -251,11 +261,11 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
     const int c = tid + i * kThreads;
     a_on[i] = kChunks % kThreads == 0 || c < kChunks;   // compile-time true when exact
     const int cc = a_on[i] ? c : 0;
-    const int r = cc / (kBK / 32), kc = cc % (kBK / 32);
+    const int r = cc / kCPR, kc = cc % kCPR;
     const int64_t arow = row0 + min(r, rows - 1);
-    a_cp[i] = prm.a_codes + arow * kb2 + 16 * kc;
-    a_sp[i] = prm.a_sf + arow * kb16 + 2 * kc;
-    a_lds[i] = r * kLdA + 32 * kc;
+    a_cp[i] = prm.a_codes + arow * kb2 + (kCE / 2) * kc;
+    a_sp[i] = prm.a_sf + arow * kb16 + (kCE / 16) * kc;
+    a_lds[i] = r * kLdA + kCE * kc;
   }
 
   f32x16_t acc[kMBa][2];
@@ -266,7 +276,7 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
 
   // Register rings (kRing slots) for the packed codes of A and B: step kt's
   // loads are issued kRing - 1 steps before their use.
-  u32x4 a_raw[kRing][kChunksPerThread];
+  araw_t a_raw[kRing][kChunksPerThread];
   uint32_t a_sraw[kRing][kChunksPerThread];
   u32x4 b_raw[kRing][2][kVec];    // [slot][block][16-byte piece]
   uint32_t b_sraw[kRing][2];      // [slot][block]: kBK/32 scale bytes
@@ -276,8 +286,11 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < kChunksPerThread; ++i) {
       if (!a_on[i]) continue;
-      a_raw[slot][i] = *reinterpret_cast<const u32x4*>(a_cp[i] + (int64_t)kt * (kBK / 2));
-      a_sraw[slot][i] = *reinterpret_cast<const uint16_t*>(a_sp[i] + (int64_t)kt * (kBK / 16));
+      a_raw[slot][i] = *reinterpret_cast<const araw_t*>(a_cp[i] + (int64_t)kt * (kBK / 2));
+      if constexpr (kCE == 32)
+        a_sraw[slot][i] = *reinterpret_cast<const uint16_t*>(a_sp[i] + (int64_t)kt * (kBK / 16));
+      else
+        a_sraw[slot][i] = a_sp[i][(int64_t)kt * (kBK / 16)];
     }
   };
   // dequantise the A step held in register slot `slot` into LDS buffer `buf`
@@ -288,12 +301,15 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
     for (int i = 0; i < kChunksPerThread; ++i) {
       if (!a_on[i]) continue;
       const half2_t sp = scales_f16<false>(a_sraw[slot][i]);
-      const half2_t s0 = bcast_lo(sp), s1 = bcast_hi(sp);
+      const half2_t s0 = bcast_lo(sp);
       half8_t* dst = reinterpret_cast<half8_t*>(base + a_lds[i]);
       dst[0] = dequant8(a_raw[slot][i].x, s0);
       dst[1] = dequant8(a_raw[slot][i].y, s0);
-      dst[2] = dequant8(a_raw[slot][i].z, s1);
-      dst[3] = dequant8(a_raw[slot][i].w, s1);
+      if constexpr (kCE == 32) {
+        const half2_t s1 = bcast_hi(sp);
+        dst[2] = dequant8(a_raw[slot][i].z, s1);
+        dst[3] = dequant8(a_raw[slot][i].w, s1);
+      }
     }
   };
   auto load_b = [&](int kt, auto slotc) {
@@ -581,9 +597,12 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream) {
   prm.E = a.E; prm.K = a.H; prm.N_w = 2 * a.I; prm.I = a.I;
   prm.out_gscale = a.out_gscale; prm.out_codes = a.out_codes; prm.out_sf = a.out_sf;
   prm.c1_dbg = a.c1_dbg; prm.h_dbg = a.h_dbg;
+  if (a.P >= 32 * a.E) {
+    prm.n_tiles = (a.I + 32 * kG1Waves - 1) / (32 * kG1Waves);
+    return launch<kG1Waves, kG1MB, kG1BK, true, kG1Ring, kG1Occ>(prm, a.P, stream);
+  }
   constexpr int kWaves = 4;
   prm.n_tiles = (a.I + 32 * kWaves - 1) / (32 * kWaves);
-  if (a.P >= 32 * a.E) return launch<kWaves, kG1MB, kG1BK, true, kG1Ring, kG1Occ>(prm, a.P, stream);
   return launch<kWaves, 1, kG1BK, true, 3, 2>(prm, a.P, stream);
 }
 
