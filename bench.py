@@ -38,7 +38,9 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="prefill", choices=["prefill", "decode"])
+    ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "stack"])
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode sub-measurement of the prefill run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=64)
@@ -124,74 +126,179 @@ def measured_traffic():
         return None
 
 
-def build_layer(w, torch, M):
+def build_layer(w, torch, M, layer=0):
     """Seeded bf16 expert weights -> NVFP4 with the library's quantiser;
-    activation scales calibrated with the library's kernels."""
+    activation scales calibrated with the library's kernels on the layer's
+    unbiased calibration batch."""
     import synthetic as S
     t0 = time.time()
-    w13_bits, w2_bits = S.expert_weights(w)
+    w13_bits, w2_bits = S.expert_weights(w, layer=layer)
     w13 = M.bf16_tensor(w13_bits)
     w2 = M.bf16_tensor(w2_bits)
     del w13_bits, w2_bits
     w13c, w13s, w13s2 = M.quantize_expert_weights(w13)
     w2c, w2s, w2s2 = M.quantize_expert_weights(w2)
     del w13, w2
-    xc, lc = S.calibration_batch(w)
+    xc, lc = S.calibration_batch(w, layer=layer)
     cal = M.calibrate_layer(w13c, w13s, w13s2, w2c, w2s, w2s2, M.bf16_tensor(xc),
                             torch.from_numpy(lc).cuda(), w.k)
-    layer = M.NVFP4MoELayer(w13c, w13s, w13s2, w2c, w2s, w2s2, cal.w13_input_scale,
-                            cal.w2_input_scale, cal.written13, cal.written2)
+    lay = M.NVFP4MoELayer(w13c, w13s, w13s2, w2c, w2s, w2s2, cal.w13_input_scale,
+                          cal.w2_input_scale, cal.written13, cal.written2)
     torch.cuda.synchronize()
-    log(f"layer prepared in {time.time() - t0:.1f}s")
-    return layer
+    log(f"{w.name} layer {layer} prepared in {time.time() - t0:.1f}s")
+    return lay
 
 
-def bench_layer(args, torch, M, L, events):
-    import synthetic as S
-    w = S.WORKLOADS[args.workload]
-    layer = build_layer(w, torch, M)
-    sets = []
-    for i in range(3):
-        x = M.bf16_tensor(S.activations(w, layer=i))
-        lg = torch.from_numpy(S.router_logits(w, layer=i)).cuda()
-        sets.append((x, lg, torch.empty_like(x)))
-    wstruct = layer.weights()
-    ws = layer.workspace(w.T, w.k)
-    nbytes = ws.numel()
+def time_steps(torch, L, events, runs, steps, warmup, T, k, stage_events=True):
+    """Time `steps` calls of nvfp4_moe_forward cycling over `runs` (list of
+    (weights, workspace tensor, x, logits, out)); HIP events on torch's
+    current stream, which the library launches on.  Returns (ms per step,
+    host wall s, per-stage µs or None)."""
     stream = torch.cuda.current_stream().cuda_stream
+    nst = len(L.MOE_STAGES)
+    evs = [events.create(nst + 1) for _ in range(steps)] if stage_events else None
+    dbgs = ([L.MoEDebug(stage_events=ctypes.cast(e, ctypes.POINTER(ctypes.c_void_p)))
+             for e in evs] if stage_events else None)
 
     def step(i, dbg=None):
-        x, lg, out = sets[i % 3]
-        L.moe_forward(wstruct, x, lg, w.T, w.k, None, out, ws, nbytes, dbg, stream)
+        wst, ws, x, lg, out = runs[i % len(runs)]
+        L.moe_forward(wst, x, lg, T, k, None, out, ws, ws.numel(), dbg, stream)
 
-    # Every timed step also records HIP events between its launches (on the
-    # library's stream), so the per-kernel times come from the timed region.
-    nst = len(L.MOE_STAGES)
-    evs = [events.create(nst + 1) for _ in range(args.steps)]
-    dbgs = [L.MoEDebug(stage_events=ctypes.cast(e, ctypes.POINTER(ctypes.c_void_p))) for e in evs]
-
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     ev = events.create(2)
     events.record(ev[0], stream)
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, dbgs[i])
+    for i in range(steps):
+        step(i, dbgs[i] if stage_events else None)
     events.record(ev[1], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_total = events.elapsed_ms(ev[0], ev[1])
+    ms_step = events.elapsed_ms(ev[0], ev[1]) / steps
     events.destroy(ev)
-    ms_step = ms_total / args.steps
+    stage_us = None
+    if stage_events:
+        stage_ms = np.zeros(nst)
+        for e in evs:
+            for s_ in range(nst):
+                stage_ms[s_] += events.elapsed_ms(e[s_], e[s_ + 1])
+            events.destroy(e)
+        stage_us = {name: 1000.0 * v / steps for name, v in zip(L.MOE_STAGES, stage_ms)}
+    return ms_step, wall, stage_us
 
-    stage_ms = np.zeros(nst)
-    for e in evs:
-        for s in range(nst):
-            stage_ms[s] += events.elapsed_ms(e[s], e[s + 1])
-        events.destroy(e)
-    stage_us = {name: 1000.0 * v / args.steps for name, v in zip(L.MOE_STAGES, stage_ms)}
-    return w, layer, ms_step, wall, stage_us
+
+def bench_layer(args, torch, M, L, events, w, layer):
+    """The layer on three rotating seeded input sets of workload w.  Every
+    timed step also records HIP events between its launches, so the
+    per-kernel times come from the timed region."""
+    import synthetic as S
+    wst = layer.weights()
+    ws = layer.workspace(w.T, w.k)
+    runs = []
+    for i in range(3):
+        x = M.bf16_tensor(S.activations(w, layer=i))
+        lg = torch.from_numpy(S.router_logits(w, layer=i)).cuda()
+        runs.append((wst, ws, x, lg, torch.empty_like(x)))
+    return time_steps(torch, L, events, runs, args.steps, args.warmup, w.T, w.k)
+
+
+def bench_decode(args, torch, M, L, events, layers):
+    """16-token decode on two alternating layers (weights > last-level
+    cache), three input sets each: tokens/s and the w13 GEMM's weight-
+    streaming rate (NVFP4 bytes of the experts the batch hits)."""
+    import synthetic as S
+    w = S.WORKLOADS["decode"]
+    runs, hits = [], []
+    for li, lay in enumerate(layers):
+        wst = lay.weights()
+        ws = lay.workspace(w.T, w.k)
+        for i in range(3):
+            x = M.bf16_tensor(S.activations(w, layer=i))
+            lg_np = S.router_logits(w, layer=i)
+            hits.append(int(np.unique(np.argsort(-lg_np, axis=1, kind="stable")[:, :w.k]).size))
+            runs.append((wst, ws, x, torch.from_numpy(lg_np).cuda(), torch.empty_like(x)))
+    # order: layer 0 set 0, layer 1 set 0, ... so consecutive steps switch weights
+    order = [runs[li * 3 + i] for i in range(3) for li in range(len(layers))]
+    hit_order = [hits[li * 3 + i] for i in range(3) for li in range(len(layers))]
+    steps = max(args.steps, 200)
+    ms, wall, st = time_steps(torch, L, events, order, steps, args.warmup, w.T, w.k)
+    n_hit = float(np.mean(hit_order))
+    per_expert = 2 * w.I * w.H * 9 // 16 + w.H * w.I * 9 // 16       # w13 + w2 codes+scales
+    g1_bytes = n_hit * (2 * w.I * w.H * 9 // 16)
+    g1 = st["gemm1_w13"]
+    return dict(workload=f"decode MoE layer: {w.T} tokens, hidden {w.H}, {w.E} experts, "
+                         f"intermediate {w.I}, top-{w.k}; 2 alternating layers x 3 input sets",
+                tokens_per_s=round(w.T / (ms * 1e-3), 1), us_per_step=round(ms * 1000, 2),
+                experts_hit=round(n_hit, 1),
+                weight_bytes_per_step=int(n_hit * per_expert),
+                layer_weight_gbps=round(n_hit * per_expert / (ms * 1e-3) / 1e9, 1),
+                gemm1_weight_gbps=round(g1_bytes / (g1 * 1e-6) / 1e9, 1),
+                gemm1_frac_of_hbm_peak=round(g1_bytes / (g1 * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                stages_us={k_: round(v, 2) for k_, v in st.items()})
+
+
+def bench_stack(args, torch, M, L, events):
+    """The 30-layer stack: x_{l+1} = bf16(x_l + MoE_l(x_l)), each layer with
+    its own weights, scales and Zipf router; 8192 tokens.  Times whole
+    passes over the stack."""
+    import synthetic as S
+    w = S.WORKLOADS["stack"]
+    layers = [build_layer(w, torch, M, layer=l) for l in range(w.layers)]
+    wsts = [lay.weights() for lay in layers]
+    nbytes = max(L.moe_workspace_size(w.T, w.k, wst) for wst in wsts)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    logits = [torch.from_numpy(S.router_logits(w, layer=l)).cuda() for l in range(w.layers)]
+    x0 = M.bf16_tensor(S.activations(w, layer=0))
+    bufs = [torch.empty_like(x0), torch.empty_like(x0)]
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def one_pass():
+        x = x0
+        for l in range(w.layers):
+            out = bufs[l % 2]
+            L.moe_forward(wsts[l], x, logits[l], w.T, w.k, x, out, ws, nbytes, None, stream)
+            x = out
+        return x
+
+    one_pass()
+    torch.cuda.synchronize()
+    passes = 3
+    ev = events.create(2)
+    events.record(ev[0], stream)
+    for _ in range(passes):
+        one_pass()
+    events.record(ev[1], stream)
+    torch.cuda.synchronize()
+    ms = events.elapsed_ms(ev[0], ev[1]) / passes
+    events.destroy(ev)
+    flops = 6.0 * w.T * w.k * w.H * w.I * w.layers
+    tflops = flops / (ms * 1e-3) / 1e12
+    return w, dict(ms_per_stack=round(ms, 3), tokens_per_s=round(w.T / (ms * 1e-3), 1),
+                   layer_tokens_per_s=round(w.T * w.layers / (ms * 1e-3), 1),
+                   expert_gemm_flops=flops, tflops_whole_stack=round(tflops, 1),
+                   frac_of_f16_peak=round(tflops / MFMA_F16_PEAK_TFLOPS, 4), passes=passes)
+
+
+def copy_ceiling(torch, events):
+    """A plain 1 GiB device-to-device copy (torch's copy kernel), timed with
+    HIP events: the practical HBM ceiling beside the 8 TB/s peak."""
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = events.create(2)
+    events.record(ev[0], stream)
+    for _ in range(10):
+        b.copy_(a)
+    events.record(ev[1], stream)
+    torch.cuda.synchronize()
+    ms = events.elapsed_ms(ev[0], ev[1]) / 10
+    events.destroy(ev)
+    del a, b
+    return round(2 * 4 * n / (ms * 1e-3) / 1e9, 1)
 
 
 def bench_quantizer(args, torch, M, L, events):
@@ -304,50 +411,73 @@ def main():
     from nvfp4_w4a4_expert_amd import moe as M
     events = HipEvents()
 
-    w, layer, ms_step, wall, stage_us = bench_layer(args, torch, M, L, events)
-    tokens_per_s = w.T / (ms_step * 1e-3)
-    log(f"layer: {ms_step * 1000:.1f} us/step, {tokens_per_s:.4g} tokens/s; stages {stage_us}")
-
-    P = w.T * w.k
-    flops_gemm1 = 2.0 * P * (2 * w.I) * w.H
-    flops_gemm2 = 2.0 * P * w.H * w.I
-    if args.workload == "prefill":
-        g1 = stage_us["gemm1_w13"]
-        ach = flops_gemm1 / (g1 * 1e-6) / 1e12
-        roofline = dict(kernel="grouped_gemm_kernel<true> (w13 + SiLU*mul + requant)",
-                        bound="mfma", achieved=round(ach, 1), peak=MFMA_F16_PEAK_TFLOPS,
-                        unit="TFLOP/s", frac=round(ach / MFMA_F16_PEAK_TFLOPS, 4),
-                        traffic=measured_traffic(),
-                        algorithmic_flops=flops_gemm1, us_per_launch=round(g1, 2))
+    import synthetic as S
+    decode = copy_gbps = quant = cpu = None
+    if args.workload == "stack":
+        w, st = bench_stack(args, torch, M, L, events)
+        ms_step, wall, stage_us = st["ms_per_stack"], None, None
+        tokens_per_s = st["tokens_per_s"]
+        log(f"stack: {st}")
+        roofline = dict(kernel="whole stack (30 layers, every kernel) vs expert-GEMM flops",
+                        bound="mfma", achieved=st["tflops_whole_stack"],
+                        peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s", frac=st["frac_of_f16_peak"],
+                        traffic=None, algorithmic_flops=st["expert_gemm_flops"])
+        gemms = None
+        extra = dict(stack=st)
     else:
-        # weight streaming: algorithmic bytes = NVFP4 w13 of every expert hit
-        # (codes + E4M3 scales) + A1 read + A2 written
-        import synthetic as S
-        ids = np.argsort(-S.router_logits(w, layer=0), axis=1, kind="stable")[:, :w.k]
-        n_hit = int(np.unique(ids).size)
-        g1 = stage_us["gemm1_w13"]
-        nbytes = n_hit * (2 * w.I) * w.H * 9 // 16 + P * w.H * 9 // 16 + P * w.I * 9 // 16
-        ach = nbytes / (g1 * 1e-6) / 1e9
-        roofline = dict(kernel="grouped_gemm_kernel<true> (w13 + SiLU*mul + requant)",
-                        bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
-                        frac=round(ach / HBM_PEAK_GBPS, 4), traffic=None,
-                        algorithmic_bytes=int(nbytes), experts_hit=n_hit,
-                        us_per_launch=round(g1, 2))
-    gemm_us = stage_us["gemm1_w13"] + stage_us["gemm2_w2"]
-    gemms = dict(us=round(gemm_us, 2),
-                 tflops=round((flops_gemm1 + flops_gemm2) / (gemm_us * 1e-6) / 1e12, 1),
-                 frac_of_f16_peak=round((flops_gemm1 + flops_gemm2) / (gemm_us * 1e-6) / 1e12
-                                        / MFMA_F16_PEAK_TFLOPS, 4))
+        # the prefill and decode layers share one layer (weights and scales)
+        layer = build_layer(S.WORKLOADS["decode"], torch, M)
+        if args.workload == "prefill":
+            w = S.WORKLOADS["prefill"]
+            ms_step, wall, stage_us = bench_layer(args, torch, M, L, events, w, layer)
+            tokens_per_s = w.T / (ms_step * 1e-3)
+            log(f"layer: {ms_step * 1000:.1f} us/step, {tokens_per_s:.4g} tokens/s; "
+                f"stages {stage_us}")
+            P = w.T * w.k
+            flops_gemm1 = 2.0 * P * (2 * w.I) * w.H
+            flops_gemm2 = 2.0 * P * w.H * w.I
+            g1 = stage_us["gemm1_w13"]
+            ach = flops_gemm1 / (g1 * 1e-6) / 1e12
+            roofline = dict(kernel="grouped_gemm_kernel<true> (w13 + SiLU*mul + requant)",
+                            bound="mfma", achieved=round(ach, 1), peak=MFMA_F16_PEAK_TFLOPS,
+                            unit="TFLOP/s", frac=round(ach / MFMA_F16_PEAK_TFLOPS, 4),
+                            traffic=measured_traffic(),
+                            algorithmic_flops=flops_gemm1, us_per_launch=round(g1, 2))
+            gemm_us = stage_us["gemm1_w13"] + stage_us["gemm2_w2"]
+            tf = (flops_gemm1 + flops_gemm2) / (gemm_us * 1e-6) / 1e12
+            gemms = dict(us=round(gemm_us, 2), tflops=round(tf, 1),
+                         frac_of_f16_peak=round(tf / MFMA_F16_PEAK_TFLOPS, 4))
+            if not args.no_decode:
+                second = build_layer(S.WORKLOADS["decode"], torch, M, layer=1)
+                decode = bench_decode(args, torch, M, L, events, [layer, second])
+                log(f"decode: {decode}")
+                del second
+        else:                                             # decode
+            w = S.WORKLOADS["decode"]
+            second = build_layer(w, torch, M, layer=1)
+            decode = bench_decode(args, torch, M, L, events, [layer, second])
+            log(f"decode: {decode}")
+            ms_step, wall, stage_us = decode["us_per_step"] / 1000.0, None, decode["stages_us"]
+            tokens_per_s = decode["tokens_per_s"]
+            g1 = stage_us["gemm1_w13"]
+            roofline = dict(kernel="grouped_gemm_kernel<true> (w13, weight streaming)",
+                            bound="hbm", achieved=decode["gemm1_weight_gbps"],
+                            peak=HBM_PEAK_GBPS, unit="GB/s",
+                            frac=decode["gemm1_frac_of_hbm_peak"], traffic=None,
+                            experts_hit=decode["experts_hit"], us_per_launch=round(g1, 2))
+            gemms = None
+        extra = dict(decode=decode)
+        del layer
 
-    quant = None
-    if not args.no_quantizer:
-        quant = bench_quantizer(args, torch, M, L, events)
-        log(f"quantizer: {quant}")
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args, w)
-        log(f"cpu baseline: {cpu}")
+    if args.workload == "prefill":
+        if not args.no_quantizer:
+            quant = bench_quantizer(args, torch, M, L, events)
+            log(f"quantizer: {quant}")
+        copy_gbps = copy_ceiling(torch, events)
+        log(f"device copy: {copy_gbps} GB/s (read + write)")
+        if not args.no_cpu_baseline:
+            cpu = cpu_baseline(args, w)
+            log(f"cpu baseline: {cpu}")
 
     rec = {
         "metric": METRIC,
@@ -363,18 +493,22 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {
-            "workload": (f"{args.workload} MoE layer: {w.T} tokens, hidden {w.H}, {w.E} experts, "
+            "workload": (("30-layer MoE stack" if args.workload == "stack" else
+                          f"{args.workload} MoE layer") +
+                         f": {w.T} tokens, hidden {w.H}, {w.E} experts, "
                          f"intermediate {w.I}, top-{w.k}, NVFP4 W4A4 (E2M1 + E4M3/16 + fp32), "
                          f"fp16 MFMA over exactly dequantised operands, fp32 accumulate"),
             "tokens": w.T, "hidden": w.H, "experts": w.E, "inter": w.I, "topk": w.k,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "stages_us": {k: round(v, 2) for k, v in stage_us.items()} if stage_us else None,
         "expert_gemms": gemms,
         "quantizer": quant,
-        "host_wall_s": round(wall, 4),
+        "hbm_copy_gbps": copy_gbps,
+        "host_wall_s": round(wall, 4) if wall is not None else None,
     }
+    rec.update(extra)
     print(json.dumps(rec), flush=True)
 
 
