@@ -73,7 +73,7 @@ NVFP4_API const char* nvfp4_status_string(nvfp4_status_t status);
 
 /* ABI revision of this header; bumped on any incompatible change. */
 NVFP4_API int32_t nvfp4_abi_version(void);
-#define NVFP4_ABI_VERSION 1
+#define NVFP4_ABI_VERSION 2
 
 /*
  * nvfp4_validate_scales — the load-time completeness check (page 3, "ROOT
@@ -195,14 +195,18 @@ NVFP4_API nvfp4_status_t nvfp4_expert_absmax(const void* x_bf16, int64_t ldx, in
                                              nvfp4_stream_t stream);
 
 /*
- * nvfp4_selftest_conversions — device self-check of the three gfx950
+ * nvfp4_selftest_conversions — device self-check of the five gfx950
  * conversion instructions the kernels use, each against a reference built
  * from the format definitions (page 3, "NVFP4" section: the E2M1 code table;
  * encoding rounds to nearest with ties to even and saturates to 6; E4M3 block
- * scales).  mismatches: device uint64[3], written asynchronously:
+ * scales).  mismatches: device uint64[5], written asynchronously:
  *   [0] fp32 -> E2M1 encode vs midpoint comparisons, every non-NaN fp32 input;
  *   [1] E2M1 byte -> fp16 pair vs the code table, all 256 bytes x 4 positions;
- *   [2] E4M3 -> fp16 vs the OCP E4M3 definition, all 254 non-NaN codes.
+ *   [2] E4M3 -> fp16 vs the OCP E4M3 definition, all 254 non-NaN codes;
+ *   [3] non-negative fp32 -> E4M3 block-scale encode (clamp to 448, then the
+ *       FP8 conversion) vs nearest-even saturating rounding, every
+ *       non-negative fp32 input and +inf;
+ *   [4] E4M3 -> fp32 vs the OCP E4M3 definition, all 127 non-negative codes.
  * All three must read 0.
  */
 NVFP4_API nvfp4_status_t nvfp4_selftest_conversions(unsigned long long* mismatches,

@@ -64,6 +64,19 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   return e == 0 ? sub : nrm;
 }
 
+// The same two conversions with the gfx950 FP8 instructions (OCP E4M3):
+// values above 448 are clamped first (the instruction alone would give
+// NaN), then the conversion rounds to nearest even.  A device self-check pins
+// both to the definitions above: the encode on every non-negative fp32 input
+// and +inf, the decode on every non-negative code.
+__device__ __forceinline__ uint32_t e4m3_encode_hw(float s) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(s, kE4M3Max), 0.0f, 0, false) & 0xFFu;
+}
+
+__device__ __forceinline__ float e4m3_decode_hw(uint32_t c) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)c, 0);
+}
+
 // |v| -> E2M1 magnitude code, nearest with ties to the even code, saturating.
 // Midpoints between the magnitudes {0,.5,1,1.5,2,3,4,6}: .25 .75 1.25 1.75
 // 2.5 3.5 5; a midpoint goes to the neighbour whose code is even.
@@ -90,8 +103,8 @@ __device__ __forceinline__ BlockScale block_scale(float amax_over_6, float gs) {
 #pragma clang fp contract(off)
   BlockScale r;
   const float s = gs * amax_over_6;
-  r.sf = e4m3_encode(s);
-  const float sv = e4m3_decode(r.sf);
+  r.sf = e4m3_encode_hw(s);
+  const float sv = e4m3_decode_hw(r.sf);
   r.inv = (sv == 0.0f) ? 0.0f : fminf(gs / sv, kFltMax);
   return r;
 }

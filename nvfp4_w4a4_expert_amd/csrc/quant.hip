@@ -193,7 +193,7 @@ __device__ __forceinline__ bool same_f16(_Float16 h, float ref) {
 }
 
 __global__ __launch_bounds__(256) void conversions_selftest_kernel(unsigned long long* count) {
-  unsigned long long local = 0;
+  unsigned long long local = 0, local8 = 0;
   const uint32_t tid = blockIdx.x * blockDim.x + threadIdx.x;
   const uint32_t stride = gridDim.x * blockDim.x;
   for (uint32_t u = tid; u < 0x80000000u; u += stride) {
@@ -202,8 +202,11 @@ __global__ __launch_bounds__(256) void conversions_selftest_kernel(unsigned long
     const uint32_t hw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, f[0], f[1], 1.0f, 0) & 0xFFu;
     const uint32_t sw = e2m1_code(f[0]) | (e2m1_code(f[1]) << 4);
     local += hw != sw;
+    // E4M3 encode of a non-negative block scale (+inf included)
+    local8 += e4m3_encode_hw(f[0]) != e4m3_encode(f[0]);
   }
   if (local) atomicAdd(count, local);
+  if (local8) atomicAdd(count + 3, local8);
   if (tid < 256) {
     const uint32_t b = tid;
     unsigned long long bad = 0;
@@ -222,6 +225,9 @@ __global__ __launch_bounds__(256) void conversions_selftest_kernel(unsigned long
       const unsigned long long bad8 = !same_f16(lo.x, ref) + !same_f16(lo.y, ref) +
                                       !same_f16(hi.x, ref) + !same_f16(hi.y, ref);
       if (bad8) atomicAdd(count + 2, bad8);
+      if (b < 0x7Fu)
+        atomicAdd(count + 4, (unsigned long long)(__float_as_uint(e4m3_decode_hw(b)) !=
+                                                   __float_as_uint(e4m3_decode(b))));
     }
   }
 }
@@ -231,7 +237,7 @@ __global__ void zero_u64_kernel(unsigned long long* p, int n) {
 }
 
 hipError_t launch_conversions_selftest(unsigned long long* count, hipStream_t stream) {
-  hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(64), 0, stream, count, 3);
+  hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(64), 0, stream, count, 5);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(conversions_selftest_kernel, dim3(8192), dim3(256), 0, stream, count);

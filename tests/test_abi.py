@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = _lib()
-    assert L.abi_version() == 1
+    assert L.abi_version() == 2
     for s in range(6):
         assert L.status_string(s)
     assert "unknown" in L.status_string(99)

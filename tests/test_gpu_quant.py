@@ -129,16 +129,17 @@ def test_zero_rows_is_noop():
 
 
 def test_hardware_conversions_selftest():
-    """The three conversion instructions behind the codes and the GEMM
-    operands equal references built from the format definitions: E2M1 encode
-    on every non-NaN fp32 input, E2M1 -> fp16 on every byte, E4M3 -> fp16 on
-    every non-NaN code."""
+    """The conversion instructions behind the codes, the block scales and the
+    GEMM operands equal references built from the format definitions: E2M1
+    encode on every non-NaN fp32 input, E2M1 -> fp16 on every byte, E4M3 ->
+    fp16 on every non-NaN code, E4M3 block-scale encode on every non-negative
+    fp32 input and +inf, E4M3 -> fp32 on every non-negative code."""
     torch = _torch()
     from nvfp4_w4a4_expert_amd import _lib as L
-    cnt = torch.full((3,), 12345, dtype=torch.int64, device="cuda")
+    cnt = torch.full((5,), 12345, dtype=torch.int64, device="cuda")
     L.selftest_conversions(cnt)
     torch.cuda.synchronize()
-    assert cnt.cpu().tolist() == [0, 0, 0]
+    assert cnt.cpu().tolist() == [0, 0, 0, 0, 0]
 
 
 def _pack_reference(codes, sf, bk):
