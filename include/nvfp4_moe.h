@@ -139,6 +139,22 @@ NVFP4_API nvfp4_status_t nvfp4_quantize_experts(const void* x_bf16, int64_t ldx,
                                                 int32_t num_dst_rows, nvfp4_stream_t stream);
 
 /*
+ * nvfp4_quantize_experts_fp16 — the same quantiser for fp16 source rows
+ * (page 3, "NVFP4" runtime-order figure: the hidden state entering the
+ * quantiser is BF16 or FP16).  Every fp16 value converts exactly to fp32, so
+ * the arithmetic above applies unchanged.  Arguments, layouts, ownership and
+ * errors as for nvfp4_quantize_experts, with x_fp16 device fp16
+ * [num_rows, ldx], 16-byte aligned, ldx % 8 == 0.
+ */
+NVFP4_API nvfp4_status_t nvfp4_quantize_experts_fp16(const void* x_fp16, int64_t ldx,
+                                                     int32_t num_rows, int32_t K, int32_t topk,
+                                                     const int32_t* expert_idx,
+                                                     const int32_t* dst_row, int32_t num_experts,
+                                                     const float* gscale, uint8_t* codes,
+                                                     uint8_t* sf, int32_t num_dst_rows,
+                                                     nvfp4_stream_t stream);
+
+/*
  * nvfp4_route_topk — the router's choice of expert_idx (page 3, "NVFP4"
  * runtime figure: the router has fixed expert_idx before quantisation) and
  * the routing weights the final sum uses ("矩阵融合" pipeline figure).
@@ -193,6 +209,32 @@ NVFP4_API nvfp4_status_t nvfp4_expert_absmax(const void* x_bf16, int64_t ldx, in
                                              const int32_t* expert_offsets, int32_t num_experts,
                                              int32_t num_rows, float* amax_out,
                                              nvfp4_stream_t stream);
+
+/*
+ * nvfp4_calibrate_input_scales — the calibration pass behind the per-expert
+ * FP32 activation scales, with its coverage report (page 3, "ROOT CAUSE":
+ * experts that saw no calibration token are left without a written
+ * input_scale; "NVFP4" section: the stored global scale is based on the
+ * 6 x 448 = 2688 range).  Over the grouped rows of each expert (as in
+ * nvfp4_expert_absmax):
+ *     input_scale[e] = fl32(max|x| / 2688), written[e] = 1   if e has rows,
+ *     input_scale[e] = NaN,                 written[e] = 0   otherwise.
+ * Passing both arrays to nvfp4_validate_scales then rejects exactly the
+ * experts without calibration rows (NVFP4_SLOT_UNWRITTEN), before any
+ * reciprocal is taken.
+ *
+ *   x_bf16, ldx, K, src, src_div, expert_offsets, num_experts, num_rows:
+ *                    as for nvfp4_expert_absmax.
+ *   input_scale_out  device fp32 [num_experts].
+ *   written_out      device uint8 [num_experts].
+ */
+NVFP4_API nvfp4_status_t nvfp4_calibrate_input_scales(const void* x_bf16, int64_t ldx, int32_t K,
+                                                      const int32_t* src, int32_t src_div,
+                                                      const int32_t* expert_offsets,
+                                                      int32_t num_experts, int32_t num_rows,
+                                                      float* input_scale_out,
+                                                      uint8_t* written_out,
+                                                      nvfp4_stream_t stream);
 
 /*
  * nvfp4_selftest_conversions — device self-check of the five gfx950

@@ -58,9 +58,11 @@ _SIGS = {
     "nvfp4_abi_version": (_i32, []),
     "nvfp4_validate_scales": (_i32, [_p, _p, _i32, _p, _p, _p]),
     "nvfp4_quantize_experts": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _p, _i32, _p, _p, _p, _i32, _p]),
+    "nvfp4_quantize_experts_fp16": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _p, _i32, _p, _p, _p, _i32, _p]),
     "nvfp4_route_topk": (_i32, [_p, _i32, _i32, _i32, _p, _p, _p]),
     "nvfp4_permute": (_i32, [_p, _i32, _i32, _i32, _p, _p, _p, _p]),
     "nvfp4_expert_absmax": (_i32, [_p, _i64, _i32, _p, _i32, _p, _i32, _i32, _p, _p]),
+    "nvfp4_calibrate_input_scales": (_i32, [_p, _i64, _i32, _p, _i32, _p, _i32, _i32, _p, _p, _p]),
     "nvfp4_selftest_conversions": (_i32, [_p, _p]),
     "nvfp4_moe_pack_weights": (_i32, [_i32, _p, _p, _i32, _i32, _i32, _p, _p, _p]),
     "nvfp4_moe_workspace_size": (_i32, [_i32, _i32, ctypes.POINTER(MoEWeights), ctypes.POINTER(ctypes.c_size_t)]),
@@ -132,6 +134,14 @@ def quantize_experts(x, ldx: int, num_rows: int, K: int, topk: int, expert_idx, 
            "nvfp4_quantize_experts")
 
 
+def quantize_experts_fp16(x, ldx: int, num_rows: int, K: int, topk: int, expert_idx, dst_row,
+                          num_experts: int, gscale, codes, sf, num_dst_rows: int, stream=None):
+    _check(_lib.nvfp4_quantize_experts_fp16(_ptr(x), ldx, num_rows, K, topk, _ptr(expert_idx),
+                                            _ptr(dst_row), num_experts, _ptr(gscale),
+                                            _ptr(codes), _ptr(sf), num_dst_rows, _stream(stream)),
+           "nvfp4_quantize_experts_fp16")
+
+
 def route_topk(logits, num_tokens: int, num_experts: int, k: int, ids, weights, stream=None):
     _check(_lib.nvfp4_route_topk(_ptr(logits), num_tokens, num_experts, k, _ptr(ids),
                                  _ptr(weights), _stream(stream)), "nvfp4_route_topk")
@@ -148,6 +158,16 @@ def expert_absmax(x, ldx: int, K: int, src, src_div: int, expert_offsets, num_ex
     _check(_lib.nvfp4_expert_absmax(_ptr(x), ldx, K, _ptr(src), src_div, _ptr(expert_offsets),
                                     num_experts, num_rows, _ptr(amax_out), _stream(stream)),
            "nvfp4_expert_absmax")
+
+
+def calibrate_input_scales(x, ldx: int, K: int, src, src_div: int, expert_offsets,
+                           num_experts: int, num_rows: int, input_scale_out, written_out,
+                           stream=None):
+    _check(_lib.nvfp4_calibrate_input_scales(_ptr(x), ldx, K, _ptr(src), src_div,
+                                             _ptr(expert_offsets), num_experts, num_rows,
+                                             _ptr(input_scale_out), _ptr(written_out),
+                                             _stream(stream)),
+           "nvfp4_calibrate_input_scales")
 
 
 def selftest_conversions(mismatches, stream=None):

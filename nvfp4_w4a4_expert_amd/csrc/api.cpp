@@ -127,6 +127,24 @@ NVFP4_API nvfp4_status_t nvfp4_quantize_experts(const void* x_bf16, int64_t ldx,
                                        num_dst_rows, static_cast<hipStream_t>(stream)));
 }
 
+NVFP4_API nvfp4_status_t nvfp4_quantize_experts_fp16(const void* x_fp16, int64_t ldx,
+                                                     int32_t num_rows, int32_t K, int32_t topk,
+                                                     const int32_t* expert_idx,
+                                                     const int32_t* dst_row, int32_t num_experts,
+                                                     const float* gscale, uint8_t* codes,
+                                                     uint8_t* sf, int32_t num_dst_rows,
+                                                     nvfp4_stream_t stream) {
+  if (num_rows < 0 || K <= 0 || K % 16 || topk < 1 || num_experts < 1 || num_dst_rows < 0 ||
+      ldx < K || ldx % 8)
+    return NVFP4_ERR_INVALID_ARG;
+  if (num_rows == 0) return NVFP4_OK;
+  if (!x_fp16 || !codes || !sf || !aligned(x_fp16, 16) || !aligned(codes, 8))
+    return NVFP4_ERR_INVALID_ARG;
+  return device_status(launch_quantize(static_cast<const uint16_t*>(x_fp16), ldx, num_rows, K,
+                                       topk, expert_idx, dst_row, num_experts, gscale, codes, sf,
+                                       num_dst_rows, static_cast<hipStream_t>(stream), true));
+}
+
 NVFP4_API nvfp4_status_t nvfp4_route_topk(const float* logits, int32_t num_tokens,
                                           int32_t num_experts, int32_t k, int32_t* ids,
                                           float* weights, nvfp4_stream_t stream) {
@@ -163,6 +181,23 @@ NVFP4_API nvfp4_status_t nvfp4_expert_absmax(const void* x_bf16, int64_t ldx, in
   return device_status(launch_absmax(static_cast<const uint16_t*>(x_bf16), ldx, K, src, src_div,
                                      expert_offsets, num_experts, num_rows, amax_out,
                                      static_cast<hipStream_t>(stream)));
+}
+
+NVFP4_API nvfp4_status_t nvfp4_calibrate_input_scales(const void* x_bf16, int64_t ldx, int32_t K,
+                                                      const int32_t* src, int32_t src_div,
+                                                      const int32_t* expert_offsets,
+                                                      int32_t num_experts, int32_t num_rows,
+                                                      float* input_scale_out,
+                                                      uint8_t* written_out,
+                                                      nvfp4_stream_t stream) {
+  if (K <= 0 || K % 8 || ldx < K || ldx % 8 || src_div < 1 || num_experts < 1 || num_rows < 0)
+    return NVFP4_ERR_INVALID_ARG;
+  if (!expert_offsets || !input_scale_out || !written_out) return NVFP4_ERR_INVALID_ARG;
+  if (num_rows > 0 && (!x_bf16 || !aligned(x_bf16, 16))) return NVFP4_ERR_INVALID_ARG;
+  return device_status(launch_calibrate(static_cast<const uint16_t*>(x_bf16), ldx, K, src,
+                                        src_div, expert_offsets, num_experts, num_rows,
+                                        input_scale_out, written_out,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 NVFP4_API nvfp4_status_t nvfp4_selftest_conversions(unsigned long long* mismatches,

@@ -11,7 +11,7 @@ namespace nvfp4 {
 hipError_t launch_quantize(const uint16_t* x, int64_t ldx, int32_t num_rows, int32_t K,
                            int32_t topk, const int32_t* expert_idx, const int32_t* dst_row,
                            int32_t num_experts, const float* gscale, uint8_t* codes, uint8_t* sf,
-                           int32_t num_dst_rows, hipStream_t stream);
+                           int32_t num_dst_rows, hipStream_t stream, bool fp16_input = false);
 
 hipError_t launch_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* ids,
                         float* weights, hipStream_t stream);
@@ -22,6 +22,10 @@ hipError_t launch_permute(const int32_t* ids, int32_t P, int32_t E, int32_t* off
 hipError_t launch_absmax(const uint16_t* x, int64_t ldx, int32_t K, const int32_t* src,
                          int32_t src_div, const int32_t* offsets, int32_t E, int32_t num_rows,
                          float* amax, hipStream_t stream);
+
+hipError_t launch_calibrate(const uint16_t* x, int64_t ldx, int32_t K, const int32_t* src,
+                            int32_t src_div, const int32_t* offsets, int32_t E, int32_t num_rows,
+                            float* scale, uint8_t* written, hipStream_t stream);
 
 hipError_t launch_conversions_selftest(unsigned long long* count, hipStream_t stream);
 

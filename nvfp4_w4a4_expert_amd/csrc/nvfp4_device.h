@@ -151,6 +151,16 @@ __device__ __forceinline__ void unpack_bf16x8(const u32x4& u, float* x) {
   x[6] = bf16_lo(u.w); x[7] = bf16_hi(u.w);
 }
 
+// Unpack 8 fp16 held in a 16-byte vector into floats (exact conversions).
+__device__ __forceinline__ void unpack_f16x8(const u32x4& u, float* x) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xFFFFu));
+    x[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+  }
+}
+
 __device__ __forceinline__ void unpack_bf16x8(const uint4& v, float* x) {
   x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
   x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);

@@ -14,8 +14,9 @@
 
 namespace nvfp4 {
 
-// kE / kP / kG: expert_idx / dst_row / gscale are present (not null).
-template <bool kE, bool kP, bool kG>
+// kE / kP / kG: expert_idx / dst_row / gscale are present (not null);
+// kF16: the source rows are fp16 instead of bf16 (both convert exactly to fp32).
+template <bool kE, bool kP, bool kG, bool kF16>
 __global__ __launch_bounds__(1024) void quantize_experts_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int32_t num_rows, int32_t nblk, int32_t topk,
     const int32_t* __restrict__ expert_idx, const int32_t* __restrict__ dst_row,
@@ -35,8 +36,13 @@ __global__ __launch_bounds__(1024) void quantize_experts_kernel(
     const u32x4* src = reinterpret_cast<const u32x4*>(x + (int64_t)t * ldx + (int64_t)b * 16);
     const u32x4 v0 = __builtin_nontemporal_load(src);
     const u32x4 v1 = __builtin_nontemporal_load(src + 1);
-    unpack_bf16x8(v0, xv);
-    unpack_bf16x8(v1, xv + 8);
+    if constexpr (kF16) {
+      unpack_f16x8(v0, xv);
+      unpack_f16x8(v1, xv + 8);
+    } else {
+      unpack_bf16x8(v0, xv);
+      unpack_bf16x8(v1, xv + 8);
+    }
     a6 = absmax16(xv) / kE2M1Max;
   }
 
@@ -80,29 +86,38 @@ __global__ __launch_bounds__(1024) void quantize_experts_kernel(
 hipError_t launch_quantize(const uint16_t* x, int64_t ldx, int32_t num_rows, int32_t K,
                            int32_t topk, const int32_t* expert_idx, const int32_t* dst_row,
                            int32_t num_experts, const float* gscale, uint8_t* codes, uint8_t* sf,
-                           int32_t num_dst_rows, hipStream_t stream) {
+                           int32_t num_dst_rows, hipStream_t stream, bool fp16_input) {
   const int32_t nblk = K / 16;
   if ((int64_t)num_rows * nblk == 0) return hipSuccess;
   // 64-lane wavefronts covering the row's blocks, at most 1024 threads per
   // workgroup (longer rows take several workgroups)
   const int32_t threads = min(1024, (nblk + 63) / 64 * 64);
   const dim3 grid((uint32_t)num_rows, (uint32_t)((nblk + threads - 1) / threads));
-  const int variant = (expert_idx ? 4 : 0) | (dst_row ? 2 : 0) | (gscale ? 1 : 0);
-#define NVFP4_QUANT_CASE(v, ke, kp, kg)                                                         \
+  const int variant = (fp16_input ? 8 : 0) | (expert_idx ? 4 : 0) | (dst_row ? 2 : 0) |
+                      (gscale ? 1 : 0);
+#define NVFP4_QUANT_CASE(v, ke, kp, kg, kf)                                                     \
   case v:                                                                                       \
-    hipLaunchKernelGGL((quantize_experts_kernel<ke, kp, kg>), grid, dim3(threads), 0, stream, x,    \
-                       ldx, num_rows, nblk, topk, expert_idx, dst_row, num_experts, gscale,     \
-                       codes, sf, num_dst_rows);                                                \
+    hipLaunchKernelGGL((quantize_experts_kernel<ke, kp, kg, kf>), grid, dim3(threads), 0,       \
+                       stream, x, ldx, num_rows, nblk, topk, expert_idx, dst_row, num_experts,  \
+                       gscale, codes, sf, num_dst_rows);                                        \
     break;
   switch (variant) {
-    NVFP4_QUANT_CASE(0, false, false, false)
-    NVFP4_QUANT_CASE(1, false, false, true)
-    NVFP4_QUANT_CASE(2, false, true, false)
-    NVFP4_QUANT_CASE(3, false, true, true)
-    NVFP4_QUANT_CASE(4, true, false, false)
-    NVFP4_QUANT_CASE(5, true, false, true)
-    NVFP4_QUANT_CASE(6, true, true, false)
-    NVFP4_QUANT_CASE(7, true, true, true)
+    NVFP4_QUANT_CASE(0, false, false, false, false)
+    NVFP4_QUANT_CASE(1, false, false, true, false)
+    NVFP4_QUANT_CASE(2, false, true, false, false)
+    NVFP4_QUANT_CASE(3, false, true, true, false)
+    NVFP4_QUANT_CASE(4, true, false, false, false)
+    NVFP4_QUANT_CASE(5, true, false, true, false)
+    NVFP4_QUANT_CASE(6, true, true, false, false)
+    NVFP4_QUANT_CASE(7, true, true, true, false)
+    NVFP4_QUANT_CASE(8, false, false, false, true)
+    NVFP4_QUANT_CASE(9, false, false, true, true)
+    NVFP4_QUANT_CASE(10, false, true, false, true)
+    NVFP4_QUANT_CASE(11, false, true, true, true)
+    NVFP4_QUANT_CASE(12, true, false, false, true)
+    NVFP4_QUANT_CASE(13, true, false, true, true)
+    NVFP4_QUANT_CASE(14, true, true, false, true)
+    NVFP4_QUANT_CASE(15, true, true, true, true)
   }
 #undef NVFP4_QUANT_CASE
   return hipGetLastError();
@@ -170,7 +185,31 @@ hipError_t launch_absmax(const uint16_t* x, int64_t ldx, int32_t K, const int32_
   return hipGetLastError();
 }
 
-// Device self-check of the three conversion instructions the kernels rely
+// Calibration: per-expert input_scale = fl32(amax / 2688) from the absmax
+// pass, and the `written` mask of experts that received at least one row.
+// An expert without rows gets NaN and written = 0, so the load-time check
+// reports it as unwritten instead of a reciprocal being taken of it.
+__global__ void calibrate_finish_kernel(float* __restrict__ scale, uint8_t* __restrict__ written,
+                                        const int32_t* __restrict__ offsets, int32_t E) {
+#pragma clang fp contract(off)
+  const int32_t e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  const bool any = offsets[e + 1] > offsets[e];
+  scale[e] = any ? scale[e] / (kE2M1Max * kE4M3Max) : __builtin_nanf("");
+  written[e] = any ? 1 : 0;
+}
+
+hipError_t launch_calibrate(const uint16_t* x, int64_t ldx, int32_t K, const int32_t* src,
+                            int32_t src_div, const int32_t* offsets, int32_t E, int32_t num_rows,
+                            float* scale, uint8_t* written, hipStream_t stream) {
+  hipError_t err = launch_absmax(x, ldx, K, src, src_div, offsets, E, num_rows, scale, stream);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(calibrate_finish_kernel, dim3((E + 255) / 256), dim3(256), 0, stream, scale,
+                     written, offsets, E);
+  return hipGetLastError();
+}
+
+// Device self-check of the five conversion instructions the kernels rely
 // on, each against a reference built from the format definitions:
 //   count[0]: fp32 -> E2M1 encode (encode8) vs the midpoint comparisons of
 //             e2m1_code(), over every non-NaN fp32 pattern (each positive

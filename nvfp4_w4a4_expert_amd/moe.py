@@ -176,10 +176,11 @@ class Calibration:
 def calibrate_layer(w13c, w13s, w13s2, w2c, w2s, w2s2, x_cal: torch.Tensor,
                     logits_cal: torch.Tensor, k: int) -> Calibration:
     """Per-expert activation scales from a calibration batch, with the
-    library's kernels: w13_input_scale = fl32(amax|x| / 2688) over the rows
-    routed to each expert; w2_input_scale = fl32(amax|h| / 2688) over the same
-    rows, where h is the layer's own SiLU(gate)*up (which does not depend on
-    the a2 scale).  Experts without calibration rows stay unwritten."""
+    library's calibration pass (nvfp4_calibrate_input_scales):
+    w13_input_scale = fl32(amax|x| / 2688) over the rows routed to each
+    expert; w2_input_scale = fl32(amax|h| / 2688) over the same rows, where h
+    is the layer's own SiLU(gate)*up (which does not depend on the a2 scale).
+    Experts without calibration rows stay unwritten (NaN, written 0)."""
     dev = x_cal.device
     Tc, H = (int(s) for s in x_cal.shape)
     E = int(w13c.shape[0])
@@ -192,20 +193,19 @@ def calibrate_layer(w13c, w13s, w13s2, w2c, w2s, w2s2, x_cal: torch.Tensor,
     inv = torch.empty(P, dtype=torch.int32, device=dev)
     _lib.route_topk(logits_cal, Tc, E, k, ids, wts)
     _lib.permute(ids, Tc, k, E, offsets, src, inv)
-    amax_x = torch.empty(E, dtype=torch.float32, device=dev)
-    _lib.expert_absmax(x_cal, H, H, src, k, offsets, E, P, amax_x)
-    counts = np.diff(offsets.cpu().numpy())
-    written = (counts > 0).astype(np.uint8)
-    s13 = (amax_x.cpu().numpy() / NVFP4_RANGE).astype(np.float32)
-    s13[written == 0] = np.nan
+    s13_d = torch.empty(E, dtype=torch.float32, device=dev)
+    written_d = torch.empty(E, dtype=torch.uint8, device=dev)
+    _lib.calibrate_input_scales(x_cal, H, H, src, k, offsets, E, P, s13_d, written_d)
+    s13 = s13_d.cpu().numpy()
+    written = written_d.cpu().numpy()
     # h does not depend on a2_gscale: run the layer with placeholder unit
     # a2 scales, restricted to the written slots, and read h back.
     ones = np.ones(E, dtype=np.float32)
     s13_run = np.where(written == 1, s13, np.float32(1.0)).astype(np.float32)
     layer = NVFP4MoELayer(w13c, w13s, w13s2, w2c, w2s, w2s2, s13_run, ones, device=dev)
     _, dbg = layer.forward(x_cal, logits_cal, k, debug=True)
-    amax_h = torch.empty(E, dtype=torch.float32, device=dev)
-    _lib.expert_absmax(dbg["h"], I, I, None, 1, dbg["expert_offsets"], E, P, amax_h)
-    s2 = (amax_h.cpu().numpy() / NVFP4_RANGE).astype(np.float32)
-    s2[written == 0] = np.nan
-    return Calibration(s13, s2, written, written.copy())
+    s2_d = torch.empty(E, dtype=torch.float32, device=dev)
+    written2_d = torch.empty(E, dtype=torch.uint8, device=dev)
+    _lib.calibrate_input_scales(dbg["h"], I, I, None, 1, dbg["expert_offsets"], E, P, s2_d,
+                                written2_d)
+    return Calibration(s13, s2_d.cpu().numpy(), written, written2_d.cpu().numpy())

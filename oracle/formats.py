@@ -145,6 +145,20 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def f16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact fp32 value of IEEE binary16 bit patterns, decoded field by field:
+    (-1)^s * 2^(e-15) * (1 + m/1024) for 0 < e < 31, (-1)^s * 2^-14 * m/1024
+    for e == 0, +-inf / NaN for e == 31."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where(b >> 15, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    m = (b & 0x3FF).astype(np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        val = np.where(e == 0, m / 1024.0 * 2.0 ** -14, (1.0 + m / 1024.0) * np.exp2(e - 15.0))
+        val = np.where(e == 31, np.where(m == 0, np.inf, np.nan), val)
+    return (sign * val).astype(np.float32)
+
+
 def f64_to_bf16(a: np.ndarray) -> np.ndarray:
     """Round real values to the nearest bf16, ties to even, via exact float64
     comparison with the two neighbouring bf16 values.  Returns uint16 bits."""

@@ -32,6 +32,7 @@ import numpy as np
 from .formats import (
     E2M1_MAX,
     bf16_to_f32,
+    f16_to_f32,
     e2m1_decode_vec,
     e2m1_encode,
     e2m1_encode_exact,
@@ -107,15 +108,33 @@ def quantize_bf16_rows(x_bits: np.ndarray, gs_row: np.ndarray, chunk: int = 4096
     return codes, sf
 
 
-def quantize_experts(x_bits: np.ndarray, row_expert: np.ndarray, gscale):
+def quantize_f16_rows(x_bits: np.ndarray, gs_row: np.ndarray, chunk: int = 4096):
+    """Quantise fp16 rows (uint16 bits [R, K]) with a per-row SFScaleVal (page
+    3, "NVFP4" runtime figure: the hidden state may be BF16 or FP16; each fp16
+    value is exactly an fp32 value, so the fp32 quantiser applies unchanged)."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    R, K = x_bits.shape
+    codes = np.empty((R, K // 2), dtype=np.uint8)
+    sf = np.empty((R, K // BLOCK), dtype=np.uint8)
+    gs_row = np.asarray(gs_row, dtype=np.float32)
+    for r0 in range(0, R, chunk):
+        r1 = min(R, r0 + chunk)
+        c, s = quantize_f32_rows(f16_to_f32(x_bits[r0:r1]), gs_row[r0:r1])
+        codes[r0:r1] = c
+        sf[r0:r1] = s
+    return codes, sf
+
+
+def quantize_experts(x_bits: np.ndarray, row_expert: np.ndarray, gscale, fp16: bool = False):
     """The MoE quantiser: row r uses SFScaleVal = gscale[row_expert[r]], or 1.0
-    for every row when ``gscale`` is None."""
+    for every row when ``gscale`` is None.  Rows are bf16 bit patterns, or
+    fp16 ones when ``fp16``."""
     R = x_bits.shape[0]
     if gscale is None:
         gs = np.ones(R, dtype=np.float32)
     else:
         gs = np.asarray(gscale, dtype=np.float32)[np.asarray(row_expert, dtype=np.int64)]
-    return quantize_bf16_rows(x_bits, gs)
+    return quantize_f16_rows(x_bits, gs) if fp16 else quantize_bf16_rows(x_bits, gs)
 
 
 def dequant(packed: np.ndarray, sf: np.ndarray) -> np.ndarray:

@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
     for name in ["nvfp4_validate_scales", "nvfp4_quantize_experts", "nvfp4_moe_forward",
                  "nvfp4_moe_workspace_size", "nvfp4_route_topk", "nvfp4_permute",
                  "nvfp4_expert_absmax", "nvfp4_status_string", "nvfp4_abi_version",
-                 "nvfp4_selftest_conversions", "nvfp4_moe_pack_weights"]:
+                 "nvfp4_selftest_conversions", "nvfp4_moe_pack_weights",
+                 "nvfp4_quantize_experts_fp16", "nvfp4_calibrate_input_scales"]:
         assert name in syms
 
 

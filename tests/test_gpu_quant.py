@@ -17,7 +17,7 @@ def _torch():
     return torch
 
 
-def _gpu_quantize(x_bits, K, topk, expert_idx, dst_row, gscale, num_dst_rows):
+def _gpu_quantize(x_bits, K, topk, expert_idx, dst_row, gscale, num_dst_rows, fp16=False):
     torch = _torch()
     from nvfp4_w4a4_expert_amd import _lib as L
     from nvfp4_w4a4_expert_amd import moe as M
@@ -29,7 +29,8 @@ def _gpu_quantize(x_bits, K, topk, expert_idx, dst_row, gscale, num_dst_rows):
     E = 1 if gscale is None else len(gscale)
     codes = torch.full((num_dst_rows, K // 2), 0xAB, dtype=torch.uint8, device="cuda")
     sf = torch.full((num_dst_rows, K // 16), 0xCD, dtype=torch.uint8, device="cuda")
-    L.quantize_experts(x, x_bits.shape[1], R, K, topk, ei, dr, E, gs, codes, sf, num_dst_rows)
+    fn = L.quantize_experts_fp16 if fp16 else L.quantize_experts
+    fn(x, x_bits.shape[1], R, K, topk, ei, dr, E, gs, codes, sf, num_dst_rows)
     torch.cuda.synchronize()
     return codes.cpu().numpy(), sf.cpu().numpy()
 
@@ -59,6 +60,41 @@ def test_every_bf16_pattern_every_scale():
     oc, osf = OQ.quantize_experts(x, expert, GS_SET)
     assert np.array_equal(sf, osf)
     assert np.array_equal(codes, oc)
+
+
+def test_every_fp16_pattern_every_scale():
+    """All 63,488 finite fp16 patterns through the fp16 entry point under the
+    ten SFScaleVal values: codes and scales bit-exact against the oracle's
+    fp16 path."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    bits = bits[np.isfinite(bits.view(np.float16))]
+    rng = np.random.default_rng(5)
+    arr = [bits, bits[rng.permutation(bits.size)]]
+    x = np.concatenate([a[:a.size // 256 * 256].reshape(-1, 256) for a in arr])
+    R = x.shape[0]
+    expert = np.arange(R, dtype=np.int32) % GS_SET.size
+    codes, sf = _gpu_quantize(x, 256, 1, expert, None, GS_SET, R, fp16=True)
+    oc, osf = OQ.quantize_experts(x, expert, GS_SET, fp16=True)
+    assert np.array_equal(sf, osf)
+    assert np.array_equal(codes, oc)
+
+
+def test_fp16_topk_scatter_ragged():
+    rng = np.random.default_rng(6)
+    T, K, k, E = 29, 208, 4, 6
+    x = (rng.standard_normal((T, K)) * np.exp(rng.uniform(-6, 6, (T, 1)))).astype(np.float16)
+    x_bits = x.view(np.uint16)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    gs = np.exp(rng.uniform(-3, 6, E)).astype(np.float32)
+    P = T * k
+    dst = rng.permutation(P).astype(np.int32)
+    codes, sf = _gpu_quantize(x_bits, K, k, ids.reshape(-1), dst, gs, P, fp16=True)
+    src_tok = np.empty(P, dtype=np.int64)
+    src_tok[dst] = np.arange(P) // k
+    row_exp = np.empty(P, dtype=np.int64)
+    row_exp[dst] = ids.reshape(-1)
+    oc, osf = OQ.quantize_experts(x_bits[src_tok], row_exp, gs, fp16=True)
+    assert np.array_equal(codes, oc) and np.array_equal(sf, osf)
 
 
 def test_topk_scatter_and_ragged_blocks():

@@ -162,3 +162,38 @@ def test_dequant_closed_form():
     sf = np.array([[0x38]], dtype=np.uint8)                       # 1.0
     d = Q.dequant(packed, sf)
     assert d[0, :4].tolist() == [0.5, 1.0, -6.0, 6.0]
+
+
+def test_f16_decode_matches_ieee_binary16():
+    """The oracle's field-by-field fp16 decode equals numpy's IEEE binary16
+    conversion on every pattern, and a few values fixed by the format."""
+    from oracle import formats as OF
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = b.view(np.float16).astype(np.float32)
+    got = OF.f16_to_f32(b)
+    fin = np.isfinite(ref)
+    assert np.array_equal(ref[fin].view(np.uint32), got[fin].view(np.uint32))
+    assert np.array_equal(np.isinf(ref), np.isinf(got)) and np.array_equal(np.isnan(ref), np.isnan(got))
+    assert OF.f16_to_f32(np.array([0x3C00, 0x0001, 0x7BFF, 0x8000], np.uint16)).tolist() == \
+        [1.0, 2.0 ** -24, 65504.0, -0.0]
+
+
+def test_f16_rows_quantise_like_bf16_rows_on_shared_values():
+    """Values that are both fp16 and bf16 numbers quantise identically through
+    either input path (the arithmetic after the exact conversion is shared)."""
+    from oracle import formats as OF
+    from oracle import quant as OQ
+    rng = np.random.default_rng(11)
+    # fp16 numbers whose significand fits in bf16's 8 bits, over fp16's range
+    m = rng.integers(128, 256, size=(64, 128)).astype(np.float64)
+    e = rng.integers(-14, 8, size=(64, 128)).astype(np.float64)   # normal fp16 range
+    sgn = np.where(rng.random((64, 128)) < 0.5, -1.0, 1.0)
+    vals = (sgn * m / 128.0 * np.exp2(e)).astype(np.float32)
+    f16 = vals.astype(np.float16)
+    assert np.array_equal(f16.astype(np.float32), vals)
+    bf16 = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(OF.bf16_to_f32(bf16), vals)
+    gs = np.exp(rng.uniform(-3, 3, 64)).astype(np.float32)
+    c1, s1 = OQ.quantize_f16_rows(f16.view(np.uint16), gs)
+    c2, s2 = OQ.quantize_bf16_rows(bf16, gs)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
