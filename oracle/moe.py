@@ -117,6 +117,27 @@ def grouped_gemm_ref(a_codes, a_sf, offsets, w_codes, w_sf, alpha, rows=None):
     return out
 
 
+def grouped_gemm_w16_ref(a, offsets, w_codes, w_sf, alpha, rows=None):
+    """Weight-only grouped GEMM (page 3, "Kernel Backend": the MARLIN backend
+    runs W4A16 and consumes no activation input_scale): C[p, n] = alpha[e] *
+    sum_k A[p, k] * deqW[e][n, k] for the rows p of expert e, with A the
+    16-bit activations as real values (float64)."""
+    a = np.asarray(a, dtype=np.float64)
+    E = offsets.size - 1
+    P = int(offsets[-1])
+    N = w_codes.shape[1]
+    sel = np.arange(P) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((sel.size, N), dtype=np.float64)
+    rexp = row_experts(offsets)[sel] if P else np.zeros(0, dtype=np.int64)
+    for e in range(E):
+        m = np.nonzero(rexp == e)[0]
+        if m.size == 0:
+            continue
+        W = dequant(w_codes[e], w_sf[e])
+        out[m] = np.float64(alpha[e]) * (a[sel[m]] @ W.T)
+    return out
+
+
 def silu_mul(c1: np.ndarray, I: int) -> np.ndarray:
     """h = silu(gate) * up, gate = columns [0, I), up = columns [I, 2I);
     silu(z) = z / (1 + exp(-z))."""
@@ -252,6 +273,36 @@ def prepare_layer(w13_bits, w2_bits, x_cal_bits, logits_cal, k, threads=8) -> La
 
 
 # --- the whole layer ----------------------------------------------------------
+
+def layer_forward_w4a16(layer: Layer, x_bits, logits, k, residual_bits=None, h_from=None):
+    """The weight-only (W4A16) forward of one MoE layer (page 3, "Kernel
+    Backend" / "本案例：CUTLASS 与 Marlin": the MARLIN backend executes W4A16 and
+    sets the activation scale to None).  Activations stay bf16; the expert
+    weights are the same NVFP4 checkpoint; the GEMM scaling is the weight's
+    weight_scale_2 alone.  The activation input scales are never read.
+
+        C1 = w13_weight_scale_2[e] * x[token(p)] . deqW13[e]^T
+        h  = bf16(silu(C1[:, :I]) * C1[:, I:])
+        C2 = w2_weight_scale_2[e] * h . deqW2[e]^T
+        out[t] = bf16(residual[t] + sum_j w[t, j] * C2[inv[t*k + j]])
+
+    ``h_from`` replaces the oracle's own h (bf16 bits [P, I]) by a given one
+    (the GEMM2 reference over given operands).  Returns a dict with ids, w,
+    offsets, src_pair, inv, c1, h_bits, c2, out_f64, out_bf16."""
+    T = x_bits.shape[0]
+    E, I = layer.E, layer.I
+    ids, w = route(logits, k)
+    offsets, src_pair, inv = permute(ids, E)
+    xp = bf16_to_f32(np.asarray(x_bits)[src_pair // k])
+    c1 = grouped_gemm_w16_ref(xp, offsets, layer.w13c, layer.w13s, layer.w13s2)
+    h_bits = f64_to_bf16(silu_mul(c1, I))
+    hin = bf16_to_f32(h_bits if h_from is None else h_from)
+    c2 = grouped_gemm_w16_ref(hin, offsets, layer.w2c, layer.w2s, layer.w2s2)
+    res = None if residual_bits is None else bf16_to_f32(residual_bits)
+    out = combine_ref(c2, w, inv, T, k, res)
+    return dict(ids=ids, w=w, offsets=offsets, src_pair=src_pair, inv=inv, c1=c1,
+                h_bits=h_bits, c2=c2, out_f64=out, out_bf16=f64_to_bf16(out))
+
 
 def layer_forward(layer: Layer, x_bits, logits, k, residual_bits=None, a2_from=None):
     """Independent end-to-end forward of one MoE layer.

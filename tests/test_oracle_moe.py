@@ -5,6 +5,7 @@ Pinned by enumerated special values, brute force with Python ``sorted`` and
 triple loops, closed forms (all-ones / one-hot operands, silu values), and
 structural properties of the synthetic workloads.
 """
+import copy
 import math
 
 import numpy as np
@@ -265,3 +266,66 @@ def test_bad_scale_slots_recipe():
     slots = S.bad_scale_slots(S.WORKLOADS["stack"])
     assert len(slots) == 3 and len({e for _, e, _ in slots}) == 3
     assert {k for _, _, k in slots} == {"nan", "unwritten_garbage", "unwritten_neg"}
+
+
+# --- weight-only (W4A16) path ---------------------------------------------------
+
+def test_grouped_gemm_w16_brute_force():
+    rng = np.random.default_rng(21)
+    E, N, K = 3, 4, 32
+    offsets = np.array([0, 3, 3, 5], dtype=np.int32)          # expert 1 has no rows
+    a_bits = S.f32_to_bf16_bits(rng.standard_normal((5, K)).astype(np.float32))
+    a = S.bf16_bits_to_f32(a_bits)
+    wc = np.stack([_rand_nvfp4(rng, N, K)[0] for _ in range(E)])
+    ws = np.stack([_rand_nvfp4(rng, N, K)[1] for _ in range(E)])
+    alpha = np.array([0.125, 7.0, -2.0])
+    got = M.grouped_gemm_w16_ref(a, offsets, wc, ws, alpha)
+    for p in range(5):
+        e = 0 if p < 3 else 2
+        for n in range(N):
+            acc = 0.0
+            for kk in range(K):
+                byte = int(wc[e, n, kk // 2])
+                c = byte & 0xF if kk % 2 == 0 else byte >> 4
+                acc += float(a[p, kk]) * F.e2m1_decode(c) * F.e4m3_decode(int(ws[e, n, kk // 16]))
+            assert got[p, n] == pytest.approx(alpha[e] * acc, rel=1e-13, abs=1e-12)
+    assert np.array_equal(M.grouped_gemm_w16_ref(a, offsets, wc, ws, alpha, rows=[4, 1]),
+                          got[[4, 1]])
+
+
+def test_w4a16_layer_is_token_major_definition_and_ignores_input_scales():
+    w = S.WORKLOADS["tiny"]
+    w13, w2 = S.expert_weights(w)
+    xc, lc = S.calibration_batch(w)
+    layer = M.prepare_layer(w13, w2, xc, lc, w.k)
+    x = S.activations(w)
+    logits = S.router_logits(w)
+    res = S.f32_to_bf16_bits(np.linspace(-1, 1, w.T * w.H, dtype=np.float32).reshape(w.T, w.H))
+    r = M.layer_forward_w4a16(layer, x, logits, w.k, residual_bits=res)
+    # token-major definition: no permutation, no grouping
+    xf = S.bf16_bits_to_f32(x).astype(np.float64)
+    ids, wts = M.route(logits, w.k)
+    ref = S.bf16_bits_to_f32(res).astype(np.float64)
+    for t in range(w.T):
+        for j in range(w.k):
+            e = ids[t, j]
+            W13 = Q.dequant(layer.w13c[e], layer.w13s[e])
+            W2 = Q.dequant(layer.w2c[e], layer.w2s[e])
+            c1 = float(layer.w13s2[e]) * (xf[t] @ W13.T)
+            g, u = c1[:w.I], c1[w.I:]
+            hb = F.f64_to_bf16(g / (1.0 + np.exp(-g)) * u)
+            h = S.bf16_bits_to_f32(hb).astype(np.float64)
+            ref[t] += wts[t, j] * float(layer.w2s2[e]) * (h @ W2.T)
+    assert np.allclose(r["out_f64"], ref, rtol=1e-12, atol=1e-12)
+    # the activation input scales play no part
+    bad = copy.copy(layer)
+    bad.w13_input_scale = np.full_like(layer.w13_input_scale, np.nan)
+    bad.w2_input_scale = np.full_like(layer.w2_input_scale, -1.0)
+    r2 = M.layer_forward_w4a16(bad, x, logits, w.k, residual_bits=res)
+    assert np.array_equal(r2["out_bf16"], r["out_bf16"])
+    # and it tracks the unquantised-activation fp64 layer more closely than W4A4
+    r4 = M.layer_forward(layer, x, logits, w.k, residual_bits=res)
+    ref_r = ref - S.bf16_bits_to_f32(res)
+    e16 = np.linalg.norm(r["out_f64"] - S.bf16_bits_to_f32(res) - ref_r)
+    e4 = np.linalg.norm(r4["out_f64"] - S.bf16_bits_to_f32(res) - ref_r)
+    assert e16 < e4
