@@ -73,7 +73,7 @@ NVFP4_API const char* nvfp4_status_string(nvfp4_status_t status);
 
 /* ABI revision of this header; bumped on any incompatible change. */
 NVFP4_API int32_t nvfp4_abi_version(void);
-#define NVFP4_ABI_VERSION 2
+#define NVFP4_ABI_VERSION 3
 
 /*
  * nvfp4_validate_scales — the load-time completeness check (page 3, "ROOT
@@ -354,6 +354,37 @@ NVFP4_API nvfp4_status_t nvfp4_moe_forward(const nvfp4_moe_weights_t* w, const v
                                            int32_t k, const void* residual_bf16, void* out_bf16,
                                            void* workspace, size_t workspace_bytes,
                                            const nvfp4_moe_debug_t* debug, nvfp4_stream_t stream);
+
+/*
+ * Weight-only (W4A16) forward of the same layer (page 3, "Kernel Backend" and
+ * the "本案例：CUTLASS 与 Marlin" comparison: the MARLIN backend runs NVFP4
+ * expert weights against bf16 activations — W4A16 — and sets the activation
+ * scale to None, so w13_input_scale / w2_input_scale are never consumed).
+ * Same weights and packed layout as nvfp4_moe_forward; on `stream`:
+ *   route -> permute ->
+ *   grouped w13 GEMM on bf16 rows, C1 = w13_scale2[e] * x[token(p)] . W13[e]^T
+ *   -> h = bf16(silu(gate) * up), kept as bf16 ->
+ *   grouped w2 GEMM, C2 = w2_scale2[e] * h . W2[e]^T (fp32) -> combine as in
+ *   nvfp4_moe_forward.
+ * Weight operands are dequantised exactly (E2M1 x E4M3 is a bf16 number);
+ * activations are used as given.  w->w13_input_scale, w2_input_scale,
+ * a1_gscale and a2_gscale may be NULL and are not read, so a layer whose
+ * activation scales fail nvfp4_validate_scales still runs here.
+ * Arguments and requirements as for nvfp4_moe_forward, with the workspace
+ * from nvfp4_moe_workspace_size_w4a16.  debug: topk_ids, topk_weights,
+ * expert_offsets, src_pair, inv_pair, c1, h, c2 are filled; the a1/a2 members
+ * are ignored; stage event 3 follows event 2 directly (no quantisation).
+ */
+NVFP4_API nvfp4_status_t nvfp4_moe_workspace_size_w4a16(int32_t num_tokens, int32_t k,
+                                                        const nvfp4_moe_weights_t* w,
+                                                        size_t* bytes);
+NVFP4_API nvfp4_status_t nvfp4_moe_forward_w4a16(const nvfp4_moe_weights_t* w,
+                                                 const void* x_bf16, const float* router_logits,
+                                                 int32_t num_tokens, int32_t k,
+                                                 const void* residual_bf16, void* out_bf16,
+                                                 void* workspace, size_t workspace_bytes,
+                                                 const nvfp4_moe_debug_t* debug,
+                                                 nvfp4_stream_t stream);
 
 #ifdef __cplusplus
 }

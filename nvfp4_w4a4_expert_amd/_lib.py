@@ -68,6 +68,10 @@ _SIGS = {
     "nvfp4_moe_workspace_size": (_i32, [_i32, _i32, ctypes.POINTER(MoEWeights), ctypes.POINTER(ctypes.c_size_t)]),
     "nvfp4_moe_forward": (_i32, [ctypes.POINTER(MoEWeights), _p, _p, _i32, _i32, _p, _p, _p,
                                  ctypes.c_size_t, ctypes.POINTER(MoEDebug), _p]),
+    "nvfp4_moe_workspace_size_w4a16": (_i32, [_i32, _i32, ctypes.POINTER(MoEWeights),
+                                              ctypes.POINTER(ctypes.c_size_t)]),
+    "nvfp4_moe_forward_w4a16": (_i32, [ctypes.POINTER(MoEWeights), _p, _p, _i32, _i32, _p, _p,
+                                       _p, ctypes.c_size_t, ctypes.POINTER(MoEDebug), _p]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -195,3 +199,21 @@ def moe_forward(weights: MoEWeights, x, router_logits, num_tokens: int, k: int, 
                                   num_tokens, k, _ptr(residual), _ptr(out), _ptr(workspace),
                                   workspace_bytes, None if debug is None else ctypes.byref(debug),
                                   _stream(stream)), "nvfp4_moe_forward")
+
+
+def moe_workspace_size_w4a16(num_tokens: int, k: int, weights: MoEWeights) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.nvfp4_moe_workspace_size_w4a16(num_tokens, k, ctypes.byref(weights),
+                                               ctypes.byref(n)),
+           "nvfp4_moe_workspace_size_w4a16")
+    return int(n.value)
+
+
+def moe_forward_w4a16(weights: MoEWeights, x, router_logits, num_tokens: int, k: int, residual,
+                      out, workspace, workspace_bytes: int, debug: Optional[MoEDebug] = None,
+                      stream=None):
+    _check(_lib.nvfp4_moe_forward_w4a16(ctypes.byref(weights), _ptr(x), _ptr(router_logits),
+                                        num_tokens, k, _ptr(residual), _ptr(out),
+                                        _ptr(workspace), workspace_bytes,
+                                        None if debug is None else ctypes.byref(debug),
+                                        _stream(stream)), "nvfp4_moe_forward_w4a16")

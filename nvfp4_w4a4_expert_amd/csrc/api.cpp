@@ -24,12 +24,15 @@ nvfp4_status_t device_status(hipError_t e) {
 }
 
 // Byte layout of the forward pass's workspace.
+// (The weight-only forward keeps no quantised activations: its a1/a2 regions
+// are empty and h holds the bf16 GEMM1 output instead.)
 struct Layout {
-  size_t ids, wts, offsets, src_pair, inv, a1c, a1s, a2c, a2s, c2, total;
+  size_t ids, wts, offsets, src_pair, inv, a1c, a1s, a2c, a2s, h, c2, total;
 };
 
-Layout layout(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I) {
+Layout layout(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I, bool w16 = false) {
   const int64_t P = T * k;
+  const int64_t Pq = w16 ? 0 : P, Ph = w16 ? P : 0;
   Layout L;
   size_t o = 0;
   L.ids = o;      o = align_up(o + (size_t)P * 4);
@@ -37,18 +40,22 @@ Layout layout(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I) {
   L.offsets = o;  o = align_up(o + (size_t)(E + 1) * 4);
   L.src_pair = o; o = align_up(o + (size_t)P * 4);
   L.inv = o;      o = align_up(o + (size_t)P * 4);
-  L.a1c = o;      o = align_up(o + (size_t)P * (H / 2));
-  L.a1s = o;      o = align_up(o + (size_t)P * (H / 16));
-  L.a2c = o;      o = align_up(o + (size_t)P * (I / 2));
-  L.a2s = o;      o = align_up(o + (size_t)P * (I / 16));
+  L.a1c = o;      o = align_up(o + (size_t)Pq * (H / 2));
+  L.a1s = o;      o = align_up(o + (size_t)Pq * (H / 16));
+  L.a2c = o;      o = align_up(o + (size_t)Pq * (I / 2));
+  L.a2s = o;      o = align_up(o + (size_t)Pq * (I / 16));
+  L.h = o;        o = align_up(o + (size_t)Ph * I * 2);
   L.c2 = o;       o = align_up(o + (size_t)P * H * 4);
   L.total = o;
   return L;
 }
 
-nvfp4_status_t check_weights(const nvfp4_moe_weights_t* w) {
-  if (!w || !w->w13 || !w->w13_sf || !w->w13_scale2 || !w->w2 || !w->w2_sf || !w->w2_scale2 ||
-      !w->w13_input_scale || !w->w2_input_scale || !w->a1_gscale || !w->a2_gscale)
+// The activation scales (input scales and their reciprocals) are required
+// by the W4A4 forward only; the weight-only forward never reads them.
+nvfp4_status_t check_weights(const nvfp4_moe_weights_t* w, bool w16 = false) {
+  if (!w || !w->w13 || !w->w13_sf || !w->w13_scale2 || !w->w2 || !w->w2_sf || !w->w2_scale2)
+    return NVFP4_ERR_INVALID_ARG;
+  if (!w16 && (!w->w13_input_scale || !w->w2_input_scale || !w->a1_gscale || !w->a2_gscale))
     return NVFP4_ERR_INVALID_ARG;
   if (w->num_experts <= 0 || w->hidden <= 0 || w->inter <= 0) return NVFP4_ERR_INVALID_ARG;
   if (w->hidden % 16 || w->inter % 16) return NVFP4_ERR_INVALID_ARG;
@@ -231,12 +238,26 @@ NVFP4_API nvfp4_status_t nvfp4_moe_workspace_size(int32_t num_tokens, int32_t k,
   return NVFP4_OK;
 }
 
-NVFP4_API nvfp4_status_t nvfp4_moe_forward(const nvfp4_moe_weights_t* w, const void* x_bf16,
-                                           const float* router_logits, int32_t num_tokens,
-                                           int32_t k, const void* residual_bf16, void* out_bf16,
-                                           void* workspace, size_t workspace_bytes,
-                                           const nvfp4_moe_debug_t* debug, nvfp4_stream_t stream) {
-  nvfp4_status_t st = check_weights(w);
+NVFP4_API nvfp4_status_t nvfp4_moe_workspace_size_w4a16(int32_t num_tokens, int32_t k,
+                                                        const nvfp4_moe_weights_t* w,
+                                                        size_t* bytes) {
+  if (!bytes || !w || num_tokens < 0 || k < 1) return NVFP4_ERR_INVALID_ARG;
+  if (w->num_experts <= 0 || w->hidden <= 0 || w->inter <= 0) return NVFP4_ERR_INVALID_ARG;
+  *bytes = layout(num_tokens, k, w->num_experts, w->hidden, w->inter, true).total;
+  return NVFP4_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// One MoE layer: W4A4 (w16 false) or weight-only W4A16 (w16 true).
+nvfp4_status_t moe_forward(const nvfp4_moe_weights_t* w, const void* x_bf16,
+                           const float* router_logits, int32_t num_tokens, int32_t k,
+                           const void* residual_bf16, void* out_bf16, void* workspace,
+                           size_t workspace_bytes, const nvfp4_moe_debug_t* debug,
+                           nvfp4_stream_t stream, bool w16) {
+  nvfp4_status_t st = check_weights(w, w16);
   if (st != NVFP4_OK) return st;
   const int32_t E = w->num_experts, H = w->hidden, I = w->inter;
   if (num_tokens < 0 || k < 1 || k > E) return NVFP4_ERR_INVALID_ARG;
@@ -247,7 +268,7 @@ NVFP4_API nvfp4_status_t nvfp4_moe_forward(const nvfp4_moe_weights_t* w, const v
   if (!aligned(x_bf16, 16) || !aligned(out_bf16, 16) ||
       (residual_bf16 && !aligned(residual_bf16, 16)))
     return NVFP4_ERR_INVALID_ARG;
-  const Layout L = layout(num_tokens, k, E, H, I);
+  const Layout L = layout(num_tokens, k, E, H, I, w16);
   if (!workspace || workspace_bytes < L.total || !aligned(workspace, kAlign))
     return NVFP4_ERR_WORKSPACE;
 
@@ -263,6 +284,7 @@ NVFP4_API nvfp4_status_t nvfp4_moe_forward(const nvfp4_moe_weights_t* w, const v
   uint8_t* a1s = reinterpret_cast<uint8_t*>(ws + L.a1s);
   uint8_t* a2c = reinterpret_cast<uint8_t*>(ws + L.a2c);
   uint8_t* a2s = reinterpret_cast<uint8_t*>(ws + L.a2s);
+  uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + L.h);
   float* c2 = reinterpret_cast<float*>(ws + L.c2);
 
   void** ev = debug ? debug->stage_events : nullptr;
@@ -274,7 +296,7 @@ NVFP4_API nvfp4_status_t nvfp4_moe_forward(const nvfp4_moe_weights_t* w, const v
   if (err == hipSuccess) err = mark(1);
   if (err == hipSuccess) err = launch_permute(ids, P, E, offsets, src_pair, inv, s);
   if (err == hipSuccess) err = mark(2);
-  if (err == hipSuccess)
+  if (err == hipSuccess && !w16)
     err = launch_quantize(static_cast<const uint16_t*>(x_bf16), H, T, H, k, ids, inv, E,
                           w->a1_gscale, a1c, a1s, P, s);
   if (err == hipSuccess) err = mark(3);
@@ -284,7 +306,13 @@ NVFP4_API nvfp4_status_t nvfp4_moe_forward(const nvfp4_moe_weights_t* w, const v
     g1.in_scale = w->w13_input_scale; g1.w_scale2 = w->w13_scale2; g1.out_gscale = w->a2_gscale;
     g1.offsets = offsets; g1.out_codes = a2c; g1.out_sf = a2s;
     g1.c1_dbg = debug ? debug->c1 : nullptr;
-    g1.h_dbg = debug ? debug->h : nullptr;
+    g1.h_dbg = debug && !w16 ? debug->h : nullptr;
+    if (w16) {
+      g1.w16 = true;
+      g1.a_rows = static_cast<const uint16_t*>(x_bf16);
+      g1.a_src = src_pair; g1.a_src_div = k; g1.lda = H;
+      g1.h_out = hbuf;
+    }
     g1.P = P; g1.E = E; g1.H = H; g1.I = I;
     err = launch_gemm1(g1, s);
   }
@@ -293,6 +321,7 @@ NVFP4_API nvfp4_status_t nvfp4_moe_forward(const nvfp4_moe_weights_t* w, const v
     Gemm2Args g2;
     g2.a_codes = a2c; g2.a_sf = a2s; g2.w_codes = w->w2; g2.w_sf = w->w2_sf;
     g2.in_scale = w->w2_input_scale; g2.w_scale2 = w->w2_scale2; g2.offsets = offsets;
+    if (w16) { g2.w16 = true; g2.a_rows = hbuf; }
     g2.out = c2; g2.P = P; g2.E = E; g2.H = H; g2.I = I;
     err = launch_gemm2(g2, s);
   }
@@ -307,13 +336,41 @@ NVFP4_API nvfp4_status_t nvfp4_moe_forward(const nvfp4_moe_weights_t* w, const v
     if (err == hipSuccess) err = copy_async(debug->expert_offsets, offsets, (size_t)(E + 1) * 4, s);
     if (err == hipSuccess) err = copy_async(debug->src_pair, src_pair, (size_t)P * 4, s);
     if (err == hipSuccess) err = copy_async(debug->inv_pair, inv, (size_t)P * 4, s);
-    if (err == hipSuccess) err = copy_async(debug->a1_codes, a1c, (size_t)P * (H / 2), s);
-    if (err == hipSuccess) err = copy_async(debug->a1_sf, a1s, (size_t)P * (H / 16), s);
-    if (err == hipSuccess) err = copy_async(debug->a2_codes, a2c, (size_t)P * (I / 2), s);
-    if (err == hipSuccess) err = copy_async(debug->a2_sf, a2s, (size_t)P * (I / 16), s);
+    if (!w16) {
+      if (err == hipSuccess) err = copy_async(debug->a1_codes, a1c, (size_t)P * (H / 2), s);
+      if (err == hipSuccess) err = copy_async(debug->a1_sf, a1s, (size_t)P * (H / 16), s);
+      if (err == hipSuccess) err = copy_async(debug->a2_codes, a2c, (size_t)P * (I / 2), s);
+      if (err == hipSuccess) err = copy_async(debug->a2_sf, a2s, (size_t)P * (I / 16), s);
+    } else {
+      if (err == hipSuccess) err = copy_async(debug->h, hbuf, (size_t)P * I * 2, s);
+    }
     if (err == hipSuccess) err = copy_async(debug->c2, c2, (size_t)P * H * 4, s);
   }
   return device_status(err);
+}
+
+}  // namespace
+
+extern "C" {
+
+NVFP4_API nvfp4_status_t nvfp4_moe_forward(const nvfp4_moe_weights_t* w, const void* x_bf16,
+                                           const float* router_logits, int32_t num_tokens,
+                                           int32_t k, const void* residual_bf16, void* out_bf16,
+                                           void* workspace, size_t workspace_bytes,
+                                           const nvfp4_moe_debug_t* debug, nvfp4_stream_t stream) {
+  return moe_forward(w, x_bf16, router_logits, num_tokens, k, residual_bf16, out_bf16, workspace,
+                     workspace_bytes, debug, stream, false);
+}
+
+NVFP4_API nvfp4_status_t nvfp4_moe_forward_w4a16(const nvfp4_moe_weights_t* w,
+                                                 const void* x_bf16, const float* router_logits,
+                                                 int32_t num_tokens, int32_t k,
+                                                 const void* residual_bf16, void* out_bf16,
+                                                 void* workspace, size_t workspace_bytes,
+                                                 const nvfp4_moe_debug_t* debug,
+                                                 nvfp4_stream_t stream) {
+  return moe_forward(w, x_bf16, router_logits, num_tokens, k, residual_bf16, out_bf16, workspace,
+                     workspace_bytes, debug, stream, true);
 }
 
 }  // extern "C"

@@ -48,6 +48,15 @@
 // 32 matching up rows, so SiLU*mul happens in registers and the tile's h
 // columns are requantised from LDS in blocks of 16.  GEMM2 stages each
 // 32 x 64 fp32 sub-tile in LDS and writes whole rows with 16-byte stores.
+//
+// Weight-only variant (kW16; page 3, "Kernel Backend": the Marlin backend
+// runs the same NVFP4 weights as W4A16, bf16 activations, no activation
+// scale).  A is bf16 rows — x gathered through src_pair for GEMM1, h for
+// GEMM2 — staged into LDS unchanged; B is dequantised to bf16 exactly (FP4 ->
+// fp32, times the E4M3 block scale in fp32, packed to bf16: the product has
+// at most 6 significant bits); the contraction runs on
+// v_mfma_f32_32x32x16_bf16; alpha is weight_scale_2 alone; GEMM1 writes h as
+// bf16 rows instead of requantising it.
 #include <type_traits>
 
 #include "internal.h"
@@ -60,6 +69,8 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kXcds = 8;
 
@@ -96,6 +107,18 @@ __device__ __forceinline__ half2_t scales_f16(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHi);
 }
 
+// 8 E2M1 codes -> 8 exact bf16 values scaled by the fp32 block scale `s`.
+// (The conversion's own scale operand applies only a power of two, so the
+// E4M3 scale is multiplied in fp32; every product is exact.)
+__device__ __forceinline__ bf16x8_t dequant8_bf16(uint32_t w, float s) {
+  const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0) * s;
+  const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1) * s;
+  const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2) * s;
+  const f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3) * s;
+  return bf16x8_t{(__bf16)p0.x, (__bf16)p0.y, (__bf16)p1.x, (__bf16)p1.y,
+                  (__bf16)p2.x, (__bf16)p2.y, (__bf16)p3.x, (__bf16)p3.y};
+}
+
 __device__ __forceinline__ half2_t bcast_lo(half2_t v) { return half2_t{v.x, v.x}; }
 
 // Workgroup barrier that orders LDS accesses only.  Every barrier in these
@@ -119,6 +142,12 @@ __device__ __forceinline__ half2_t bcast_hi(half2_t v) { return half2_t{v.y, v.y
 struct GemmParams {
   const uint8_t* a_codes;   // [P, K/2]
   const uint8_t* a_sf;      // [P, K/16]
+  // weight-only variant: A row p is a_rows[(a_src ? a_src[p] / a_src_div : p) * lda]
+  const uint16_t* a_rows;   // bf16
+  const int32_t* a_src;
+  int64_t lda;
+  int32_t a_src_div;
+  uint16_t* h_out;          // GEMM1: bf16 [P, I]
   const uint8_t* w_codes;   // [E, N_w, K/2]
   const uint8_t* w_sf;      // [E, N_w, K/16]
   const float* in_scale;    // [E]
@@ -139,7 +168,7 @@ struct GemmParams {
 
 }  // namespace
 
-template <int kWaves, int kMB, int kBK, bool kGated, int kRing, int kOcc>
+template <int kWaves, int kMB, int kBK, bool kGated, int kRing, int kOcc, bool kW16>
 __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
     const GemmParams prm) {
   constexpr int kThreads = 64 * kWaves;
@@ -244,12 +273,14 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
   auto tile = [&](auto mbc) {
   constexpr int kMBa = decltype(mbc)::value;
   // A is staged in chunks of 32 elements (16 code bytes + 2 scales), or of
-  // 16 elements when that is what it takes to give every thread a chunk.
-  constexpr int kCE = 32 * kMBa * (kBK / 32) >= kThreads ? 32 : 16;
+  // 16 elements when that is what it takes to give every thread a chunk;
+  // bf16 rows (kW16) in chunks of 8 elements (16 bytes).
+  constexpr int kCE = kW16 ? 8 : 32 * kMBa * (kBK / 32) >= kThreads ? 32 : 16;
   constexpr int kCPR = kBK / kCE;                        // chunks per row per step
   constexpr int kChunks = 32 * kMBa * kCPR;
   constexpr int kChunksPerThread = (kChunks + kThreads - 1) / kThreads;
-  using araw_t = std::conditional_t<kCE == 32, u32x4, u32x2>;
+  using araw_t = std::conditional_t<kW16 || kCE == 32, u32x4, u32x2>;
+  using op_t = std::conditional_t<kW16, bf16x8_t, half8_t>;
 
   // ---- A staging assignment: chunk c -> (row, kCE-wide k chunk) -------------
   const uint8_t* a_cp[kChunksPerThread];
@@ -263,8 +294,14 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
     const int cc = a_on[i] ? c : 0;
     const int r = cc / kCPR, kc = cc % kCPR;
     const int64_t arow = row0 + min(r, rows - 1);
-    a_cp[i] = prm.a_codes + arow * kb2 + (kCE / 2) * kc;
-    a_sp[i] = prm.a_sf + arow * kb16 + (kCE / 16) * kc;
+    if constexpr (kW16) {
+      const int64_t srow = prm.a_src ? prm.a_src[arow] / prm.a_src_div : arow;
+      a_cp[i] = reinterpret_cast<const uint8_t*>(prm.a_rows + srow * prm.lda + kCE * kc);
+      a_sp[i] = nullptr;
+    } else {
+      a_cp[i] = prm.a_codes + arow * kb2 + (kCE / 2) * kc;
+      a_sp[i] = prm.a_sf + arow * kb16 + (kCE / 16) * kc;
+    }
     a_lds[i] = r * kLdA + kCE * kc;
   }
 
@@ -286,6 +323,10 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < kChunksPerThread; ++i) {
       if (!a_on[i]) continue;
+      if constexpr (kW16) {
+        a_raw[slot][i] = *reinterpret_cast<const araw_t*>(a_cp[i] + (int64_t)kt * (kBK * 2));
+        continue;
+      }
       a_raw[slot][i] = *reinterpret_cast<const araw_t*>(a_cp[i] + (int64_t)kt * (kBK / 2));
       if constexpr (kCE == 32)
         a_sraw[slot][i] = *reinterpret_cast<const uint16_t*>(a_sp[i] + (int64_t)kt * (kBK / 16));
@@ -300,6 +341,10 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < kChunksPerThread; ++i) {
       if (!a_on[i]) continue;
+      if constexpr (kW16) {
+        *reinterpret_cast<u32x4*>(base + a_lds[i]) = a_raw[slot][i];
+        continue;
+      }
       const half2_t sp = scales_f16<false>(a_sraw[slot][i]);
       const half2_t s0 = bcast_lo(sp);
       half8_t* dst = reinterpret_cast<half8_t*>(base + a_lds[i]);
@@ -333,29 +378,50 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
     constexpr int buf = decltype(bufc)::value;
     const _Float16* abase = smem + lbuf * (kBM * kLdA) + (lane & 31) * kLdA + (kBK / 2) * g;
     // block scales of this step: kBK/32 per block, as fp16 pairs
+    // (8-value piece st of the lane's K range lies in block scale st / 2)
     half2_t sc[2][2];
+    float scf[2][kBK / 32];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      sc[j][0] = scales_f16<false>(b_sraw[buf][j]);
-      sc[j][1] = kBK == 128 ? scales_f16<true>(b_sraw[buf][j]) : sc[j][0];
+      if constexpr (kW16) {
+        const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)b_sraw[buf][j], false);
+        scf[j][0] = lo.x;
+        scf[j][1] = lo.y;
+        if constexpr (kBK == 128) {
+          const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)b_sraw[buf][j], true);
+          scf[j][2] = hi.x;
+          scf[j][3] = hi.y;
+        }
+      } else {
+        sc[j][0] = scales_f16<false>(b_sraw[buf][j]);
+        sc[j][1] = kBK == 128 ? scales_f16<true>(b_sraw[buf][j]) : sc[j][0];
+      }
     }
-    auto bdeq = [&](int st, int j) -> half8_t {
+    auto bdeq = [&](int st, int j) -> op_t {
       const u32x4& v = b_raw[buf][j][st >> 2];
       const uint32_t word = (st & 3) == 0 ? v.x : (st & 3) == 1 ? v.y : (st & 3) == 2 ? v.z : v.w;
-      const half2_t pair = sc[j][(st >> 2) & 1];
-      return dequant8(word, ((st >> 1) & 1) ? bcast_hi(pair) : bcast_lo(pair));
+      if constexpr (kW16) {
+        return dequant8_bf16(word, scf[j][st >> 1]);
+      } else {
+        const half2_t pair = sc[j][(st >> 2) & 1];
+        return dequant8(word, ((st >> 1) & 1) ? bcast_hi(pair) : bcast_lo(pair));
+      }
     };
-    auto aread = [&](int st, int i) -> half8_t {
-      return *reinterpret_cast<const half8_t*>(abase + i * 32 * kLdA + 8 * st);
+    auto aread = [&](int st, int i) -> op_t {
+      return *reinterpret_cast<const op_t*>(abase + i * 32 * kLdA + 8 * st);
     };
-    half8_t bf[2], af[kMBa];
+    auto mfma = [](op_t a, op_t b, f32x16_t c) -> f32x16_t {
+      if constexpr (kW16) return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+      else return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    };
+    op_t bf[2], af[kMBa];
 #pragma unroll
     for (int j = 0; j < 2; ++j) bf[j] = bdeq(0, j);
 #pragma unroll
     for (int i = 0; i < kMBa; ++i) af[i] = aread(0, i);
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
-      half8_t nbf[2], naf[kMBa];
+      op_t nbf[2], naf[kMBa];
       if (st + 1 < kSteps) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) nbf[j] = bdeq(st + 1, j);
@@ -364,8 +430,8 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
       }
 #pragma unroll
       for (int i = 0; i < kMBa; ++i) {
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[0], acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[1], acc[i][1], 0, 0, 0);
+        acc[i][0] = mfma(af[i], bf[0], acc[i][0]);
+        acc[i][1] = mfma(af[i], bf[1], acc[i][1]);
       }
       if (st + 1 < kSteps) {
 #pragma unroll
@@ -420,7 +486,7 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
   if (nkr < nk) step(nkr, Int<0>{});
   if constexpr (kRing > 2) if (nkr + 1 < nk) step(nkr + 1, Int<1>{});
 
-  const float alpha = prm.in_scale[e] * prm.w_scale2[e];
+  const float alpha = kW16 ? prm.w_scale2[e] : prm.in_scale[e] * prm.w_scale2[e];
   // MFMA 32x32 output layout: lane holds column (lane & 31) and rows
   // 8 * (i / 4) + 4 * (lane / 32) + (i % 4) for accumulator element i.
   const int ccol = lane & 31, crow = 4 * g;
@@ -505,6 +571,17 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
         }
     }
     lds_barrier();
+    if constexpr (kW16) {
+      // h rows out as bf16, 16 bytes per store
+      constexpr int kPieces = kHW / 8;
+      for (int item = tid; item < 32 * kMBa * kPieces; item += kThreads) {
+        const int row = item / kPieces, pc = item % kPieces;
+        const int32_t hcol = hbase + 8 * pc;
+        if (row < rows && hcol < I)
+          *reinterpret_cast<u32x4*>(prm.h_out + (int64_t)(row0 + row) * I + hcol) =
+              *reinterpret_cast<const u32x4*>(sh + row * kLdh + 8 * pc);
+      }
+    } else {
     // requantise: rows x (kHW / 16) blocks of 16 columns
     constexpr int kItems = 32 * kMBa * (kHW / 16);
     const float gs = prm.out_gscale[e];
@@ -525,6 +602,7 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
         *reinterpret_cast<uint2*>(prm.out_codes + p * ob2 + hcol / 2) = wv;
         prm.out_sf[p * ob16 + hcol / 16] = (uint8_t)bsc.sf;
       }
+    }
     }
   }
   };  // tile
@@ -561,7 +639,7 @@ struct Residency {
   int cus = 0, per_cu = 0;
 };
 
-template <int kWaves, int kMB, int kBK, bool kGated, int kRing, int kOcc>
+template <int kWaves, int kMB, int kBK, bool kGated, int kRing, int kOcc, bool kW16>
 hipError_t launch(GemmParams prm, int32_t P, hipStream_t stream) {
   constexpr int kBM = 32 * kMB;
   static Residency res;
@@ -571,7 +649,8 @@ hipError_t launch(GemmParams prm, int32_t P, hipStream_t stream) {
     if (err == hipSuccess) err = hipDeviceGetAttribute(&res.cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (err == hipSuccess)
       err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &res.per_cu, (const void*)grouped_gemm_kernel<kWaves, kMB, kBK, kGated, kRing, kOcc>, 64 * kWaves, 0);
+          &res.per_cu, (const void*)grouped_gemm_kernel<kWaves, kMB, kBK, kGated, kRing, kOcc, kW16>,
+          64 * kWaves, 0);
     if (err != hipSuccess) return err;
     if (res.per_cu < 1) res.per_cu = 1;
   }
@@ -579,7 +658,7 @@ hipError_t launch(GemmParams prm, int32_t P, hipStream_t stream) {
   const int64_t slots = (int64_t)res.cus * res.per_cu;
   int64_t grid = tiles < slots ? tiles : slots;
   grid = (grid + kXcds - 1) / kXcds * kXcds;            // whole XCD rounds
-  hipLaunchKernelGGL((grouped_gemm_kernel<kWaves, kMB, kBK, kGated, kRing, kOcc>), dim3((uint32_t)grid),
+  hipLaunchKernelGGL((grouped_gemm_kernel<kWaves, kMB, kBK, kGated, kRing, kOcc, kW16>), dim3((uint32_t)grid),
                      dim3(64 * kWaves), 0, stream, prm);
   return hipGetLastError();
 }
@@ -593,30 +672,39 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream) {
   if (a.P == 0) return hipSuccess;
   GemmParams prm{};
   prm.a_codes = a.a_codes; prm.a_sf = a.a_sf; prm.w_codes = a.w_codes; prm.w_sf = a.w_sf;
+  prm.a_rows = a.a_rows; prm.a_src = a.a_src; prm.a_src_div = a.a_src_div; prm.lda = a.lda;
+  prm.h_out = a.h_out;
   prm.in_scale = a.in_scale; prm.w_scale2 = a.w_scale2; prm.offsets = a.offsets;
   prm.E = a.E; prm.K = a.H; prm.N_w = 2 * a.I; prm.I = a.I;
   prm.out_gscale = a.out_gscale; prm.out_codes = a.out_codes; prm.out_sf = a.out_sf;
   prm.c1_dbg = a.c1_dbg; prm.h_dbg = a.h_dbg;
   if (a.P >= 32 * a.E) {
     prm.n_tiles = (a.I + 32 * kG1Waves - 1) / (32 * kG1Waves);
-    return launch<kG1Waves, kG1MB, kG1BK, true, kG1Ring, kG1Occ>(prm, a.P, stream);
+    if (a.w16) return launch<kG1Waves, kG1MB, kG1BK, true, kG1Ring, kG1Occ, true>(prm, a.P, stream);
+    return launch<kG1Waves, kG1MB, kG1BK, true, kG1Ring, kG1Occ, false>(prm, a.P, stream);
   }
   constexpr int kWaves = 4;
   prm.n_tiles = (a.I + 32 * kWaves - 1) / (32 * kWaves);
-  return launch<kWaves, 1, kG1BK, true, 3, 2>(prm, a.P, stream);
+  if (a.w16) return launch<kWaves, 1, kG1BK, true, 3, 2, true>(prm, a.P, stream);
+  return launch<kWaves, 1, kG1BK, true, 3, 2, false>(prm, a.P, stream);
 }
 
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream) {
   if (a.P == 0) return hipSuccess;
   GemmParams prm{};
   prm.a_codes = a.a_codes; prm.a_sf = a.a_sf; prm.w_codes = a.w_codes; prm.w_sf = a.w_sf;
+  prm.a_rows = a.a_rows; prm.lda = a.I;
   prm.in_scale = a.in_scale; prm.w_scale2 = a.w_scale2; prm.offsets = a.offsets;
   prm.E = a.E; prm.K = a.I; prm.N_w = a.H; prm.I = a.I;
   prm.c_out = a.out; prm.ldc = a.H;
   constexpr int kWaves = 4;
   prm.n_tiles = (a.H + 64 * kWaves - 1) / (64 * kWaves);
-  if (a.P >= 32 * a.E) return launch<kWaves, kG2MB, 64, false, kG2Ring, kG2Occ>(prm, a.P, stream);
-  return launch<kWaves, 1, 64, false, 3, 2>(prm, a.P, stream);
+  if (a.P >= 32 * a.E) {
+    if (a.w16) return launch<kWaves, kG2MB, 64, false, kG2Ring, kG2Occ, true>(prm, a.P, stream);
+    return launch<kWaves, kG2MB, 64, false, kG2Ring, kG2Occ, false>(prm, a.P, stream);
+  }
+  if (a.w16) return launch<kWaves, 1, 64, false, 3, 2, true>(prm, a.P, stream);
+  return launch<kWaves, 1, 64, false, 3, 2, false>(prm, a.P, stream);
 }
 
 // ---- load-time weight layout conversion -----------------------------------

@@ -32,6 +32,13 @@ hipError_t launch_conversions_selftest(unsigned long long* count, hipStream_t st
 struct Gemm1Args {
   const uint8_t* a_codes;   // [P, H/2]
   const uint8_t* a_sf;      // [P, H/16]
+  // weight-only variant (w16): A row p = a_rows[(a_src[p] / a_src_div) * lda], bf16
+  const uint16_t* a_rows = nullptr;
+  const int32_t* a_src = nullptr;
+  int64_t lda = 0;
+  int32_t a_src_div = 1;
+  uint16_t* h_out = nullptr;  // [P, I] bf16 h (w16)
+  bool w16 = false;
   const uint8_t* w_codes;   // [E, 2I, H/2]
   const uint8_t* w_sf;      // [E, 2I, H/16]
   const float* in_scale;    // [E] w13_input_scale
@@ -48,6 +55,8 @@ struct Gemm1Args {
 struct Gemm2Args {
   const uint8_t* a_codes;   // [P, I/2]
   const uint8_t* a_sf;      // [P, I/16]
+  const uint16_t* a_rows = nullptr;  // w16: bf16 h [P, I]
+  bool w16 = false;
   const uint8_t* w_codes;   // [E, H, I/2]
   const uint8_t* w_sf;      // [E, H, I/16]
   const float* in_scale;    // [E] w2_input_scale

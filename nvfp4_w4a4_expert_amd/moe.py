@@ -54,7 +54,7 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
 
 
 class NVFP4MoELayer:
-    """Device-resident NVFP4 MoE layer.
+    """Device-resident NVFP4 MoE layer (W4A4: activations quantised per expert).
 
     Weight tensors may be numpy arrays (uploaded) or device tensors, in the
     checkpoint layout: w13 [E, 2I, H/2] u8, w13_sf [E, 2I, H/16] u8,
@@ -75,6 +75,13 @@ class NVFP4MoELayer:
         st, gs2, slots, _ = _lib.validate_scales(s2, written2)
         if st != _lib.OK:
             raise BadScaleError("w2", slots)
+        self._load_weights(w13, w13_sf, w13_scale2, w2, w2_sf, w2_scale2, device)
+        self.w13_input_scale = _dev_f32(s13, device)
+        self.w2_input_scale = _dev_f32(s2, device)
+        self.a1_gscale = _dev_f32(gs1, device)
+        self.a2_gscale = _dev_f32(gs2, device)
+
+    def _load_weights(self, w13, w13_sf, w13_scale2, w2, w2_sf, w2_scale2, device):
         up8 = (lambda a: a if isinstance(a, torch.Tensor) else _dev_u8(a, device))
         up32 = (lambda a: a if isinstance(a, torch.Tensor) else _dev_f32(a, device))
         w13, w13_sf, w2, w2_sf = up8(w13), up8(w13_sf), up8(w2), up8(w2_sf)
@@ -87,22 +94,25 @@ class NVFP4MoELayer:
         _lib.moe_pack_weights(0, w13, w13_sf, self.E, self.H, self.I, self.w13, self.w13_sf)
         _lib.moe_pack_weights(1, w2, w2_sf, self.E, self.H, self.I, self.w2, self.w2_sf)
         self.w13_scale2, self.w2_scale2 = up32(w13_scale2), up32(w2_scale2)
-        self.w13_input_scale = _dev_f32(s13, device)
-        self.w2_input_scale = _dev_f32(s2, device)
-        self.a1_gscale = _dev_f32(gs1, device)
-        self.a2_gscale = _dev_f32(gs2, device)
         self.device = device
         self._ws = None
 
     def weights(self) -> _lib.MoEWeights:
+        def ptr(t):
+            return 0 if t is None else t.data_ptr()
         return _lib.MoEWeights(
             self.w13.data_ptr(), self.w13_sf.data_ptr(), self.w13_scale2.data_ptr(),
             self.w2.data_ptr(), self.w2_sf.data_ptr(), self.w2_scale2.data_ptr(),
-            self.w13_input_scale.data_ptr(), self.w2_input_scale.data_ptr(),
-            self.a1_gscale.data_ptr(), self.a2_gscale.data_ptr(), self.E, self.H, self.I)
+            ptr(self.w13_input_scale), ptr(self.w2_input_scale),
+            ptr(self.a1_gscale), ptr(self.a2_gscale), self.E, self.H, self.I)
+
+    _workspace_size = staticmethod(_lib.moe_workspace_size)
+    _forward = staticmethod(_lib.moe_forward)
+    _debug_names = ("topk_ids", "topk_weights", "expert_offsets", "src_pair", "inv_pair",
+                    "a1_codes", "a1_sf", "c1", "h", "a2_codes", "a2_sf", "c2")
 
     def workspace(self, T: int, k: int) -> torch.Tensor:
-        n = _lib.moe_workspace_size(T, k, self.weights())
+        n = self._workspace_size(T, k, self.weights())
         if self._ws is None or self._ws.numel() < n:
             self._ws = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
         return self._ws
@@ -122,23 +132,49 @@ class NVFP4MoELayer:
         if debug:
             P, H, I, E = T * k, self.H, self.I, self.E
             dev = self.device
-            bufs = dict(
-                topk_ids=torch.empty((T, k), dtype=torch.int32, device=dev),
-                topk_weights=torch.empty((T, k), dtype=torch.float32, device=dev),
-                expert_offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
-                src_pair=torch.empty(P, dtype=torch.int32, device=dev),
-                inv_pair=torch.empty(P, dtype=torch.int32, device=dev),
-                a1_codes=torch.empty((P, H // 2), dtype=torch.uint8, device=dev),
-                a1_sf=torch.empty((P, H // 16), dtype=torch.uint8, device=dev),
-                c1=torch.empty((P, 2 * I), dtype=torch.float32, device=dev),
-                h=torch.empty((P, I), dtype=torch.int16, device=dev),
-                a2_codes=torch.empty((P, I // 2), dtype=torch.uint8, device=dev),
-                a2_sf=torch.empty((P, I // 16), dtype=torch.uint8, device=dev),
-                c2=torch.empty((P, H), dtype=torch.float32, device=dev),
-            )
+            shapes = dict(
+                topk_ids=((T, k), torch.int32), topk_weights=((T, k), torch.float32),
+                expert_offsets=((E + 1,), torch.int32), src_pair=((P,), torch.int32),
+                inv_pair=((P,), torch.int32), a1_codes=((P, H // 2), torch.uint8),
+                a1_sf=((P, H // 16), torch.uint8), c1=((P, 2 * I), torch.float32),
+                h=((P, I), torch.int16), a2_codes=((P, I // 2), torch.uint8),
+                a2_sf=((P, I // 16), torch.uint8), c2=((P, H), torch.float32))
+            bufs = {name: torch.empty(shapes[name][0], dtype=shapes[name][1], device=dev)
+                    for name in self._debug_names}
             dbg = _lib.MoEDebug(**{name: t.data_ptr() for name, t in bufs.items()})
-        _lib.moe_forward(w, x, logits, T, k, residual, out, ws, ws.numel(), dbg, stream)
+        self._forward(w, x, logits, T, k, residual, out, ws, ws.numel(), dbg, stream)
         return (out, bufs) if debug else out
+
+
+class NVFP4W4A16MoELayer(NVFP4MoELayer):
+    """Weight-only (W4A16) execution of the same NVFP4 expert weights
+    (page 3, "Kernel Backend": the Marlin backend runs W4A16 and consumes no
+    activation input_scale).  Activations stay bf16; no activation scale is
+    taken, checked or read, so a checkpoint whose input scales fail the
+    load-time check still runs here.  Same weight arguments as NVFP4MoELayer.
+    """
+
+    def __init__(self, w13, w13_sf, w13_scale2, w2, w2_sf, w2_scale2, device="cuda"):
+        self._load_weights(w13, w13_sf, w13_scale2, w2, w2_sf, w2_scale2, device)
+        self.w13_input_scale = self.w2_input_scale = None
+        self.a1_gscale = self.a2_gscale = None
+
+    @classmethod
+    def sharing(cls, layer: NVFP4MoELayer) -> "NVFP4W4A16MoELayer":
+        """A weight-only view of an existing layer's packed weights (no copy)."""
+        obj = cls.__new__(cls)
+        for name in ("E", "H", "I", "w13", "w13_sf", "w13_scale2", "w2", "w2_sf", "w2_scale2",
+                     "device"):
+            setattr(obj, name, getattr(layer, name))
+        obj.w13_input_scale = obj.w2_input_scale = None
+        obj.a1_gscale = obj.a2_gscale = None
+        obj._ws = None
+        return obj
+
+    _workspace_size = staticmethod(_lib.moe_workspace_size_w4a16)
+    _forward = staticmethod(_lib.moe_forward_w4a16)
+    _debug_names = ("topk_ids", "topk_weights", "expert_offsets", "src_pair", "inv_pair",
+                    "c1", "h", "c2")
 
 
 # --- producing a layer with the library's kernels ----------------------------

@@ -82,11 +82,18 @@ def device_layer(layer: OM.Layer):
                            layer.written13, layer.written2, device="cuda")
 
 
-def run_forward(layer: OM.Layer, x_bits, logits, k, residual_bits=None):
+def device_layer_w4a16(layer: OM.Layer):
+    """The weight-only layer: weights only, no activation scale passed."""
+    from nvfp4_w4a4_expert_amd import moe as M
+    return M.NVFP4W4A16MoELayer(layer.w13c, layer.w13s, layer.w13s2, layer.w2c, layer.w2s,
+                                layer.w2s2, device="cuda")
+
+
+def run_forward(layer: OM.Layer, x_bits, logits, k, residual_bits=None, w4a16=False):
     """GPU forward with every intermediate dumped; returns numpy arrays."""
     import torch
     from nvfp4_w4a4_expert_amd import moe as M
-    dl = device_layer(layer)
+    dl = device_layer_w4a16(layer) if w4a16 else device_layer(layer)
     x = M.bf16_tensor(x_bits)
     lg = torch.from_numpy(np.ascontiguousarray(logits, dtype=np.float32)).cuda()
     res = None if residual_bits is None else M.bf16_tensor(residual_bits)
@@ -159,3 +166,51 @@ def check_layer_parity(layer: OM.Layer, x_bits, logits, k, residual_bits=None, l
                 out_max=float(outr.max()), out_median=float(np.median(outr)),
                 out_vs_rounded_max=float(out_vs_rounded.max()),
                 e2e_max=float(e2e.max()), a2_byte_diffs_vs_own=a2_flips, got=got, ref=ref)
+
+
+def check_layer_parity_w4a16(layer: OM.Layer, x_bits, logits, k, residual_bits=None, label=""):
+    """Stage-by-stage parity of one weight-only (W4A16) GPU forward against
+    the oracle's layer_forward_w4a16.  Routing and permutation exactly; C1
+    per row within REL_L2_TOL of the fp64 product of the bf16 x rows and the
+    dequantised weights; h correctly rounded from the fp64 SiLU*mul; C2
+    against the fp64 product over the GPU's own h (one bf16 rounding may
+    differ from the oracle's); the output correctly rounded from that C2's
+    combine."""
+    T = x_bits.shape[0]
+    I = layer.I
+    progress(f"{label}: GPU W4A16 forward")
+    got = run_forward(layer, x_bits, logits, k, residual_bits, w4a16=True)
+    progress(f"{label}: oracle W4A16 forward")
+    ref = OM.layer_forward_w4a16(layer, x_bits, logits, k, residual_bits)
+    progress(f"{label}: comparing")
+
+    assert np.array_equal(got["topk_ids"], ref["ids"]), label + " routing ids"
+    wrel = np.abs(got["topk_weights"] - ref["w"]) / np.abs(ref["w"])
+    assert wrel.max() < 2e-6, (label, "routing weights", wrel.max())
+    assert np.array_equal(got["expert_offsets"], ref["offsets"]), label + " offsets"
+    assert np.array_equal(got["src_pair"], ref["src_pair"]), label + " src_pair"
+    assert np.array_equal(got["inv_pair"], ref["inv"]), label + " inv_pair"
+
+    c1 = rel_l2_rows(got["c1"], ref["c1"])
+    assert c1.max() <= REL_L2_TOL, (label, "C1", c1.max())
+    h_exact = OM.silu_mul(ref["c1"], I)
+    h_gpu = bf16_f64(got["h"])
+    assert_correctly_rounded_bf16(h_gpu, h_exact, label + " h")
+    hr = rel_l2_rows(h_gpu, h_exact)
+
+    progress(f"{label}: oracle W4A16 GEMM2 over the GPU's h")
+    c2_ref = OM.grouped_gemm_w16_ref(OF.bf16_to_f32(got["h"]), ref["offsets"], layer.w2c,
+                                     layer.w2s, layer.w2s2)
+    c2 = rel_l2_rows(got["c2"], c2_ref)
+    assert c2.max() <= REL_L2_TOL, (label, "C2", c2.max())
+
+    res = None if residual_bits is None else OF.bf16_to_f32(residual_bits)
+    out_ref = OM.combine_ref(c2_ref, ref["w"], ref["inv"], T, k, res)
+    out_gpu = bf16_f64(got["out"])
+    assert_correctly_rounded_bf16(out_gpu, out_ref, label + " out")
+    outr = rel_l2_rows(out_gpu, out_ref)
+    e2e = rel_l2_rows(out_gpu, ref["out_f64"])
+    h_diffs = int(np.count_nonzero(got["h"] != ref["h_bits"]))
+    return dict(c1_max=float(c1.max()), h_max=float(hr.max()), c2_max=float(c2.max()),
+                out_max=float(outr.max()), out_median=float(np.median(outr)),
+                e2e_max=float(e2e.max()), h_diffs_vs_own=h_diffs, got=got, ref=ref)

@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
                  "nvfp4_moe_workspace_size", "nvfp4_route_topk", "nvfp4_permute",
                  "nvfp4_expert_absmax", "nvfp4_status_string", "nvfp4_abi_version",
                  "nvfp4_selftest_conversions", "nvfp4_moe_pack_weights",
-                 "nvfp4_quantize_experts_fp16", "nvfp4_calibrate_input_scales"]:
+                 "nvfp4_quantize_experts_fp16", "nvfp4_calibrate_input_scales",
+                 "nvfp4_moe_forward_w4a16", "nvfp4_moe_workspace_size_w4a16"]:
         assert name in syms
 
 
@@ -46,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = _lib()
-    assert L.abi_version() == 2
+    assert L.abi_version() == 3
     for s in range(6):
         assert L.status_string(s)
     assert "unknown" in L.status_string(99)
@@ -139,6 +140,37 @@ def test_workspace_size_grows_with_tokens():
     assert 0 < a < b
     P = 4096 * 8
     assert b >= P * (2816 // 2 + 2816 // 16 + 704 // 2 + 704 // 16 + 2816 * 4 + 16)
+
+
+def test_w4a16_host_checks_need_no_activation_scales():
+    L = _lib()
+    f = L._lib
+    fake = 4096
+    # weights present, all four activation-scale pointers NULL
+    w = L.MoEWeights(*([fake] * 6), 0, 0, 0, 0, 4, 256, 128)
+    # the W4A4 forward requires them, the weight-only forward does not
+    assert f.nvfp4_moe_forward(ctypes.byref(w), fake, fake, 4, 2, None, fake, fake, 1 << 30,
+                               None, None) == L.ERR_INVALID_ARG
+    assert f.nvfp4_moe_forward_w4a16(ctypes.byref(w), fake, fake, 4, 2, None, fake, None, 0,
+                                     None, None) == L.ERR_WORKSPACE
+    assert f.nvfp4_moe_forward_w4a16(ctypes.byref(w), None, None, 0, 2, None, None, None, 0,
+                                     None, None) == L.OK
+    w13_missing = L.MoEWeights(0, *([fake] * 5), 0, 0, 0, 0, 4, 256, 128)
+    assert f.nvfp4_moe_forward_w4a16(ctypes.byref(w13_missing), fake, fake, 4, 2, None, fake,
+                                     fake, 1 << 30, None, None) == L.ERR_INVALID_ARG
+    w.inter = 96
+    assert f.nvfp4_moe_forward_w4a16(ctypes.byref(w), fake, fake, 4, 2, None, fake, fake,
+                                     1 << 30, None, None) == L.ERR_UNSUPPORTED
+
+
+def test_w4a16_workspace_holds_bf16_h_instead_of_codes():
+    L = _lib()
+    w = L.MoEWeights(*([0] * 10), 128, 2816, 704)
+    P = 4096 * 8
+    b = L.moe_workspace_size_w4a16(4096, 8, w)
+    assert b >= P * (704 * 2 + 2816 * 4 + 16)
+    assert b < L.moe_workspace_size(4096, 8, w) + P * 704 * 2
+    assert b - P * (704 * 2 + 2816 * 4 + 16) < 8 * 256 + 129 * 4
 
 
 def test_bad_scales_are_rejected_before_upload():
