@@ -73,7 +73,7 @@ NVFP4_API const char* nvfp4_status_string(nvfp4_status_t status);
 
 /* ABI revision of this header; bumped on any incompatible change. */
 NVFP4_API int32_t nvfp4_abi_version(void);
-#define NVFP4_ABI_VERSION 3
+#define NVFP4_ABI_VERSION 4
 
 /*
  * nvfp4_validate_scales — the load-time completeness check (page 3, "ROOT
@@ -385,6 +385,62 @@ NVFP4_API nvfp4_status_t nvfp4_moe_forward_w4a16(const nvfp4_moe_weights_t* w,
                                                  void* workspace, size_t workspace_bytes,
                                                  const nvfp4_moe_debug_t* debug,
                                                  nvfp4_stream_t stream);
+
+/*
+ * ---- UE8M0 (MX-style) block-scale mode --------------------------------------
+ * Page 3 ("NVFP4" section, quantiser excerpt) instantiates the per-expert
+ * quantiser with a UE8M0_SF switch that selects UE8M0 (unsigned 8-bit
+ * power-of-two exponent) block scales instead of E4M3.  The pages give only
+ * the switch; this library's reading: the block-scale value is formed as in
+ * the E4M3 mode, s = fl32(gs * fl32(amax / 6)), and encoded as the smallest
+ * power of two >= s, code = log2 + 127 clamped to [1, 254]; a block is 32
+ * consecutive elements; elements are normalised by fl32(gs / 2^(code-127))
+ * (clamped to FLT_MAX) and rounded to E2M1 exactly as in the E4M3 mode.
+ * Dequantised value: E2M1(code) * 2^(sf - 127) (times the FP32 global scale).
+ */
+
+/*
+ * nvfp4_quantize_experts_mx — nvfp4_quantize_experts in the UE8M0 mode.  Same
+ * arguments and behaviour, except: K % 32 == 0, and sf is [num_dst_rows, K/32]
+ * UE8M0 codes (one per 32 elements).
+ */
+NVFP4_API nvfp4_status_t nvfp4_quantize_experts_mx(const void* x_bf16, int64_t ldx,
+                                                   int32_t num_rows, int32_t K, int32_t topk,
+                                                   const int32_t* expert_idx,
+                                                   const int32_t* dst_row, int32_t num_experts,
+                                                   const float* gscale, uint8_t* codes,
+                                                   uint8_t* sf, int32_t num_dst_rows,
+                                                   nvfp4_stream_t stream);
+
+/*
+ * nvfp4_moe_pack_weights_mx — nvfp4_moe_pack_weights for UE8M0 weights:
+ * scales are [E, 2I, H/32] (projection 0) or [E, H, I/32] (projection 1);
+ * codes as in the E4M3 mode.  Same requirements and errors.
+ */
+NVFP4_API nvfp4_status_t nvfp4_moe_pack_weights_mx(int32_t projection, const uint8_t* codes,
+                                                   const uint8_t* sf, int32_t num_experts,
+                                                   int32_t hidden, int32_t inter,
+                                                   uint8_t* codes_out, uint8_t* sf_out,
+                                                   nvfp4_stream_t stream);
+
+/*
+ * nvfp4_moe_forward_mx — the W4A4 layer of nvfp4_moe_forward with every block
+ * scale in the UE8M0 mode: weights packed by nvfp4_moe_pack_weights_mx, A1 and
+ * A2 quantised with UE8M0 scales per 32 elements (a1_gscale / a2_gscale as
+ * SFScaleVal), both grouped GEMMs on the gfx950 scaled FP4 matrix instruction
+ * (the power-of-two block scales are applied by the instruction; nothing is
+ * dequantised), alpha = input_scale * weight_scale_2 as in the E4M3 mode.
+ * Same arguments, requirements, workspace (nvfp4_moe_workspace_size) and
+ * debug buffers as nvfp4_moe_forward; debug a1_sf / a2_sf receive [P, H/32]
+ * and [P, I/32] UE8M0 codes.
+ */
+NVFP4_API nvfp4_status_t nvfp4_moe_forward_mx(const nvfp4_moe_weights_t* w, const void* x_bf16,
+                                              const float* router_logits, int32_t num_tokens,
+                                              int32_t k, const void* residual_bf16,
+                                              void* out_bf16, void* workspace,
+                                              size_t workspace_bytes,
+                                              const nvfp4_moe_debug_t* debug,
+                                              nvfp4_stream_t stream);
 
 #ifdef __cplusplus
 }

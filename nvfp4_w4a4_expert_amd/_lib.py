@@ -68,6 +68,10 @@ _SIGS = {
     "nvfp4_moe_workspace_size": (_i32, [_i32, _i32, ctypes.POINTER(MoEWeights), ctypes.POINTER(ctypes.c_size_t)]),
     "nvfp4_moe_forward": (_i32, [ctypes.POINTER(MoEWeights), _p, _p, _i32, _i32, _p, _p, _p,
                                  ctypes.c_size_t, ctypes.POINTER(MoEDebug), _p]),
+    "nvfp4_quantize_experts_mx": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _p, _i32, _p, _p, _p, _i32, _p]),
+    "nvfp4_moe_pack_weights_mx": (_i32, [_i32, _p, _p, _i32, _i32, _i32, _p, _p, _p]),
+    "nvfp4_moe_forward_mx": (_i32, [ctypes.POINTER(MoEWeights), _p, _p, _i32, _i32, _p, _p, _p,
+                                    ctypes.c_size_t, ctypes.POINTER(MoEDebug), _p]),
     "nvfp4_moe_workspace_size_w4a16": (_i32, [_i32, _i32, ctypes.POINTER(MoEWeights),
                                               ctypes.POINTER(ctypes.c_size_t)]),
     "nvfp4_moe_forward_w4a16": (_i32, [ctypes.POINTER(MoEWeights), _p, _p, _i32, _i32, _p, _p,
@@ -217,3 +221,27 @@ def moe_forward_w4a16(weights: MoEWeights, x, router_logits, num_tokens: int, k:
                                         _ptr(workspace), workspace_bytes,
                                         None if debug is None else ctypes.byref(debug),
                                         _stream(stream)), "nvfp4_moe_forward_w4a16")
+
+
+def quantize_experts_mx(x, ldx: int, num_rows: int, K: int, topk: int, expert_idx, dst_row,
+                        num_experts: int, gscale, codes, sf, num_dst_rows: int, stream=None):
+    _check(_lib.nvfp4_quantize_experts_mx(_ptr(x), ldx, num_rows, K, topk, _ptr(expert_idx),
+                                          _ptr(dst_row), num_experts, _ptr(gscale), _ptr(codes),
+                                          _ptr(sf), num_dst_rows, _stream(stream)),
+           "nvfp4_quantize_experts_mx")
+
+
+def moe_pack_weights_mx(projection: int, codes, sf, num_experts: int, hidden: int, inter: int,
+                        codes_out, sf_out, stream=None):
+    _check(_lib.nvfp4_moe_pack_weights_mx(projection, _ptr(codes), _ptr(sf), num_experts, hidden,
+                                          inter, _ptr(codes_out), _ptr(sf_out), _stream(stream)),
+           "nvfp4_moe_pack_weights_mx")
+
+
+def moe_forward_mx(weights: MoEWeights, x, router_logits, num_tokens: int, k: int, residual, out,
+                   workspace, workspace_bytes: int, debug: Optional[MoEDebug] = None,
+                   stream=None):
+    _check(_lib.nvfp4_moe_forward_mx(ctypes.byref(weights), _ptr(x), _ptr(router_logits),
+                                     num_tokens, k, _ptr(residual), _ptr(out), _ptr(workspace),
+                                     workspace_bytes, None if debug is None else ctypes.byref(debug),
+                                     _stream(stream)), "nvfp4_moe_forward_mx")

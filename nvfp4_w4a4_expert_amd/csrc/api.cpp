@@ -152,6 +152,25 @@ NVFP4_API nvfp4_status_t nvfp4_quantize_experts_fp16(const void* x_fp16, int64_t
                                        num_dst_rows, static_cast<hipStream_t>(stream), true));
 }
 
+NVFP4_API nvfp4_status_t nvfp4_quantize_experts_mx(const void* x_bf16, int64_t ldx,
+                                                   int32_t num_rows, int32_t K, int32_t topk,
+                                                   const int32_t* expert_idx,
+                                                   const int32_t* dst_row, int32_t num_experts,
+                                                   const float* gscale, uint8_t* codes,
+                                                   uint8_t* sf, int32_t num_dst_rows,
+                                                   nvfp4_stream_t stream) {
+  if (num_rows < 0 || K <= 0 || K % 32 || topk < 1 || num_experts < 1 || num_dst_rows < 0 ||
+      ldx < K || ldx % 8)
+    return NVFP4_ERR_INVALID_ARG;
+  if (num_rows == 0) return NVFP4_OK;
+  if (!x_bf16 || !codes || !sf || !aligned(x_bf16, 16) || !aligned(codes, 8))
+    return NVFP4_ERR_INVALID_ARG;
+  return device_status(launch_quantize(static_cast<const uint16_t*>(x_bf16), ldx, num_rows, K,
+                                       topk, expert_idx, dst_row, num_experts, gscale, codes, sf,
+                                       num_dst_rows, static_cast<hipStream_t>(stream), false,
+                                       true));
+}
+
 NVFP4_API nvfp4_status_t nvfp4_route_topk(const float* logits, int32_t num_tokens,
                                           int32_t num_experts, int32_t k, int32_t* ids,
                                           float* weights, nvfp4_stream_t stream) {
@@ -213,10 +232,13 @@ NVFP4_API nvfp4_status_t nvfp4_selftest_conversions(unsigned long long* mismatch
   return device_status(launch_conversions_selftest(mismatches, static_cast<hipStream_t>(stream)));
 }
 
-NVFP4_API nvfp4_status_t nvfp4_moe_pack_weights(int32_t projection, const uint8_t* codes,
-                                                const uint8_t* sf, int32_t num_experts,
-                                                int32_t hidden, int32_t inter, uint8_t* codes_out,
-                                                uint8_t* sf_out, nvfp4_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+nvfp4_status_t pack_weights(int32_t projection, const uint8_t* codes, const uint8_t* sf,
+                            int32_t num_experts, int32_t hidden, int32_t inter,
+                            uint8_t* codes_out, uint8_t* sf_out, nvfp4_stream_t stream, bool mx) {
   if (projection != 0 && projection != 1) return NVFP4_ERR_INVALID_ARG;
   if (num_experts < 1 || hidden <= 0 || inter <= 0 || hidden % 16 || inter % 16)
     return NVFP4_ERR_INVALID_ARG;
@@ -227,7 +249,28 @@ NVFP4_API nvfp4_status_t nvfp4_moe_pack_weights(int32_t projection, const uint8_
   const int32_t N = projection == 0 ? 2 * inter : hidden;
   const int32_t K = projection == 0 ? hidden : inter;
   return device_status(launch_pack_weights(projection, codes, sf, num_experts, N, K, codes_out,
-                                           sf_out, static_cast<hipStream_t>(stream)));
+                                           sf_out, static_cast<hipStream_t>(stream), mx));
+}
+
+}  // namespace
+
+extern "C" {
+
+NVFP4_API nvfp4_status_t nvfp4_moe_pack_weights(int32_t projection, const uint8_t* codes,
+                                                const uint8_t* sf, int32_t num_experts,
+                                                int32_t hidden, int32_t inter, uint8_t* codes_out,
+                                                uint8_t* sf_out, nvfp4_stream_t stream) {
+  return pack_weights(projection, codes, sf, num_experts, hidden, inter, codes_out, sf_out,
+                      stream, false);
+}
+
+NVFP4_API nvfp4_status_t nvfp4_moe_pack_weights_mx(int32_t projection, const uint8_t* codes,
+                                                   const uint8_t* sf, int32_t num_experts,
+                                                   int32_t hidden, int32_t inter,
+                                                   uint8_t* codes_out, uint8_t* sf_out,
+                                                   nvfp4_stream_t stream) {
+  return pack_weights(projection, codes, sf, num_experts, hidden, inter, codes_out, sf_out,
+                      stream, true);
 }
 
 NVFP4_API nvfp4_status_t nvfp4_moe_workspace_size(int32_t num_tokens, int32_t k,
@@ -251,12 +294,17 @@ NVFP4_API nvfp4_status_t nvfp4_moe_workspace_size_w4a16(int32_t num_tokens, int3
 
 namespace {
 
-// One MoE layer: W4A4 (w16 false) or weight-only W4A16 (w16 true).
+enum class Mode { kNV, kW16, kMX };
+
+// One MoE layer: W4A4 with E4M3 scales (kNV), weight-only W4A16 (kW16), or
+// W4A4 with UE8M0 scales per 32 elements (kMX).
 nvfp4_status_t moe_forward(const nvfp4_moe_weights_t* w, const void* x_bf16,
                            const float* router_logits, int32_t num_tokens, int32_t k,
                            const void* residual_bf16, void* out_bf16, void* workspace,
                            size_t workspace_bytes, const nvfp4_moe_debug_t* debug,
-                           nvfp4_stream_t stream, bool w16) {
+                           nvfp4_stream_t stream, Mode mode) {
+  const bool w16 = mode == Mode::kW16, mx = mode == Mode::kMX;
+  const int32_t sblk = mx ? 32 : 16;                    // elements per block scale
   nvfp4_status_t st = check_weights(w, w16);
   if (st != NVFP4_OK) return st;
   const int32_t E = w->num_experts, H = w->hidden, I = w->inter;
@@ -298,7 +346,7 @@ nvfp4_status_t moe_forward(const nvfp4_moe_weights_t* w, const void* x_bf16,
   if (err == hipSuccess) err = mark(2);
   if (err == hipSuccess && !w16)
     err = launch_quantize(static_cast<const uint16_t*>(x_bf16), H, T, H, k, ids, inv, E,
-                          w->a1_gscale, a1c, a1s, P, s);
+                          w->a1_gscale, a1c, a1s, P, s, false, mx);
   if (err == hipSuccess) err = mark(3);
   if (err == hipSuccess) {
     Gemm1Args g1;
@@ -307,6 +355,7 @@ nvfp4_status_t moe_forward(const nvfp4_moe_weights_t* w, const void* x_bf16,
     g1.offsets = offsets; g1.out_codes = a2c; g1.out_sf = a2s;
     g1.c1_dbg = debug ? debug->c1 : nullptr;
     g1.h_dbg = debug && !w16 ? debug->h : nullptr;
+    g1.mx = mx;
     if (w16) {
       g1.w16 = true;
       g1.a_rows = static_cast<const uint16_t*>(x_bf16);
@@ -322,6 +371,7 @@ nvfp4_status_t moe_forward(const nvfp4_moe_weights_t* w, const void* x_bf16,
     g2.a_codes = a2c; g2.a_sf = a2s; g2.w_codes = w->w2; g2.w_sf = w->w2_sf;
     g2.in_scale = w->w2_input_scale; g2.w_scale2 = w->w2_scale2; g2.offsets = offsets;
     if (w16) { g2.w16 = true; g2.a_rows = hbuf; }
+    g2.mx = mx;
     g2.out = c2; g2.P = P; g2.E = E; g2.H = H; g2.I = I;
     err = launch_gemm2(g2, s);
   }
@@ -338,9 +388,9 @@ nvfp4_status_t moe_forward(const nvfp4_moe_weights_t* w, const void* x_bf16,
     if (err == hipSuccess) err = copy_async(debug->inv_pair, inv, (size_t)P * 4, s);
     if (!w16) {
       if (err == hipSuccess) err = copy_async(debug->a1_codes, a1c, (size_t)P * (H / 2), s);
-      if (err == hipSuccess) err = copy_async(debug->a1_sf, a1s, (size_t)P * (H / 16), s);
+      if (err == hipSuccess) err = copy_async(debug->a1_sf, a1s, (size_t)P * (H / sblk), s);
       if (err == hipSuccess) err = copy_async(debug->a2_codes, a2c, (size_t)P * (I / 2), s);
-      if (err == hipSuccess) err = copy_async(debug->a2_sf, a2s, (size_t)P * (I / 16), s);
+      if (err == hipSuccess) err = copy_async(debug->a2_sf, a2s, (size_t)P * (I / sblk), s);
     } else {
       if (err == hipSuccess) err = copy_async(debug->h, hbuf, (size_t)P * I * 2, s);
     }
@@ -359,7 +409,18 @@ NVFP4_API nvfp4_status_t nvfp4_moe_forward(const nvfp4_moe_weights_t* w, const v
                                            void* workspace, size_t workspace_bytes,
                                            const nvfp4_moe_debug_t* debug, nvfp4_stream_t stream) {
   return moe_forward(w, x_bf16, router_logits, num_tokens, k, residual_bf16, out_bf16, workspace,
-                     workspace_bytes, debug, stream, false);
+                     workspace_bytes, debug, stream, Mode::kNV);
+}
+
+NVFP4_API nvfp4_status_t nvfp4_moe_forward_mx(const nvfp4_moe_weights_t* w, const void* x_bf16,
+                                              const float* router_logits, int32_t num_tokens,
+                                              int32_t k, const void* residual_bf16,
+                                              void* out_bf16, void* workspace,
+                                              size_t workspace_bytes,
+                                              const nvfp4_moe_debug_t* debug,
+                                              nvfp4_stream_t stream) {
+  return moe_forward(w, x_bf16, router_logits, num_tokens, k, residual_bf16, out_bf16, workspace,
+                     workspace_bytes, debug, stream, Mode::kMX);
 }
 
 NVFP4_API nvfp4_status_t nvfp4_moe_forward_w4a16(const nvfp4_moe_weights_t* w,
@@ -370,7 +431,7 @@ NVFP4_API nvfp4_status_t nvfp4_moe_forward_w4a16(const nvfp4_moe_weights_t* w,
                                                  const nvfp4_moe_debug_t* debug,
                                                  nvfp4_stream_t stream) {
   return moe_forward(w, x_bf16, router_logits, num_tokens, k, residual_bf16, out_bf16, workspace,
-                     workspace_bytes, debug, stream, true);
+                     workspace_bytes, debug, stream, Mode::kW16);
 }
 
 }  // extern "C"

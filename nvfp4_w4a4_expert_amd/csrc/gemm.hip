@@ -57,6 +57,15 @@
 // at most 6 significant bits); the contraction runs on
 // v_mfma_f32_32x32x16_bf16; alpha is weight_scale_2 alone; GEMM1 writes h as
 // bf16 rows instead of requantising it.
+//
+// UE8M0 variant (kModeMX; page 3, "NVFP4" section: the quantiser template's
+// UE8M0_SF switch — power-of-two block scales, one per 32 elements).  Both
+// operands stay packed E2M1: the gfx950 scaled matrix instruction
+// v_mfma_scale_f32_32x32x64_f8f6f4 multiplies FP4 codes and applies one
+// power-of-two scale per lane per 32-element block itself, so nothing is
+// dequantised.  A's codes and scale bytes are staged in LDS as they are; the
+// same K permutation gives each lane 32 consecutive elements (one block) per
+// instruction; GEMM1 requantises h in the UE8M0 mode.
 #include <type_traits>
 
 #include "internal.h"
@@ -71,6 +80,12 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// Operand modes of the grouped GEMM.
+constexpr int kModeNV = 0;     // NVFP4 x NVFP4, fp16 MFMA on exact dequantised values
+constexpr int kModeW16 = 1;    // bf16 activations x NVFP4 weights, bf16 MFMA
+constexpr int kModeMX = 2;     // UE8M0 FP4 x UE8M0 FP4, scaled FP4 MFMA
 
 constexpr int kXcds = 8;
 
@@ -168,12 +183,21 @@ struct GemmParams {
 
 }  // namespace
 
-template <int kWaves, int kMB, int kBK, bool kGated, int kRing, int kOcc, bool kW16>
+template <int kWaves, int kMB, int kBK, bool kGated, int kRing, int kOcc, int kMode>
 __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
     const GemmParams prm) {
+  constexpr bool kW16 = kMode == kModeW16;
+  constexpr bool kMX = kMode == kModeMX;
   constexpr int kThreads = 64 * kWaves;
   constexpr int kBM = 32 * kMB;
   constexpr int kLdA = kBK + 8;                          // fp16 per LDS row (16-byte pad)
+  // UE8M0 mode LDS buffer: packed codes, rows padded by 16 bytes (the 16-byte
+  // reads of 16 consecutive rows then start on distinct 4-bank groups), then
+  // the rows' kBK/32 scale bytes
+  constexpr int kLdAb = kBK / 2 + 16;
+  constexpr int kScOff = kBM * kLdAb;
+  constexpr int kMxBuf = kScOff + kBM * (kBK / 32);
+  static_assert(!kMX || 2 * kMxBuf <= 2 * kBM * kLdA * 2, "UE8M0 stage fits the LDS buffer");
   constexpr int kVec = kBK / 64;                         // 16-byte B loads per block per step
   constexpr int kSteps = kBK / 16;                       // MFMA rounds per step
   __shared__ __align__(16) _Float16 smem[2 * kBM * kLdA];
@@ -223,7 +247,7 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5;
   const int32_t K = prm.K;
-  const int64_t kb2 = K / 2, kb16 = K / 16;
+  const int64_t kb2 = K / 2, kb16 = K / 16, kb32 = K / 32;
   const int nk = K / kBK;
 
   // ---- persistent loop over tiles; the workgroups on one XCD walk a
@@ -264,7 +288,10 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
     if (!active) blk_row0 = 0;                         // inactive waves read block 0
     const int64_t rbase = (int64_t)e * prm.N_w + blk_row0;
     b_cp[j] = prm.w_codes + rbase * kb2 + 16 * lane;
-    b_sp[j] = prm.w_sf + rbase * kb16 + (kBK / 32) * lane;
+    // scale bytes per lane per K step: kBK/32 E4M3 scales (16-element
+    // blocks) or kBK/64 UE8M0 scales (32-element blocks)
+    b_sp[j] = kMX ? prm.w_sf + rbase * kb32 + (kBK / 64) * lane
+                  : prm.w_sf + rbase * kb16 + (kBK / 32) * lane;
   }
 
   // The tile body, for kMBa = the number of 32-row sub-tiles that hold rows
@@ -274,18 +301,20 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
   constexpr int kMBa = decltype(mbc)::value;
   // A is staged in chunks of 32 elements (16 code bytes + 2 scales), or of
   // 16 elements when that is what it takes to give every thread a chunk;
-  // bf16 rows (kW16) in chunks of 8 elements (16 bytes).
-  constexpr int kCE = kW16 ? 8 : 32 * kMBa * (kBK / 32) >= kThreads ? 32 : 16;
+  // bf16 rows (kW16) in chunks of 8 elements (16 bytes); UE8M0 codes (kMX) in
+  // chunks of one 32-element block (16 code bytes + 1 scale byte).
+  constexpr int kCE = kW16 ? 8 : kMX ? 32 : 32 * kMBa * (kBK / 32) >= kThreads ? 32 : 16;
   constexpr int kCPR = kBK / kCE;                        // chunks per row per step
   constexpr int kChunks = 32 * kMBa * kCPR;
   constexpr int kChunksPerThread = (kChunks + kThreads - 1) / kThreads;
-  using araw_t = std::conditional_t<kW16 || kCE == 32, u32x4, u32x2>;
+  using araw_t = std::conditional_t<kW16 || kMX || kCE == 32, u32x4, u32x2>;
   using op_t = std::conditional_t<kW16, bf16x8_t, half8_t>;
 
   // ---- A staging assignment: chunk c -> (row, kCE-wide k chunk) -------------
   const uint8_t* a_cp[kChunksPerThread];
   const uint8_t* a_sp[kChunksPerThread];
   int a_lds[kChunksPerThread];
+  int a_lds_s[kChunksPerThread];                          // UE8M0 mode: scale byte offset
   bool a_on[kChunksPerThread];
 #pragma unroll
   for (int i = 0; i < kChunksPerThread; ++i) {
@@ -298,11 +327,15 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
       const int64_t srow = prm.a_src ? prm.a_src[arow] / prm.a_src_div : arow;
       a_cp[i] = reinterpret_cast<const uint8_t*>(prm.a_rows + srow * prm.lda + kCE * kc);
       a_sp[i] = nullptr;
+    } else if constexpr (kMX) {
+      a_cp[i] = prm.a_codes + arow * kb2 + 16 * kc;
+      a_sp[i] = prm.a_sf + arow * kb32 + kc;
     } else {
       a_cp[i] = prm.a_codes + arow * kb2 + (kCE / 2) * kc;
       a_sp[i] = prm.a_sf + arow * kb16 + (kCE / 16) * kc;
     }
-    a_lds[i] = r * kLdA + kCE * kc;
+    a_lds[i] = kMX ? r * kLdAb + 16 * kc : r * kLdA + kCE * kc;
+    a_lds_s[i] = kScOff + r * (kBK / 32) + kc;
   }
 
   f32x16_t acc[kMBa][2];
@@ -328,7 +361,9 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
         continue;
       }
       a_raw[slot][i] = *reinterpret_cast<const araw_t*>(a_cp[i] + (int64_t)kt * (kBK / 2));
-      if constexpr (kCE == 32)
+      if constexpr (kMX)
+        a_sraw[slot][i] = a_sp[i][(int64_t)kt * (kBK / 32)];
+      else if constexpr (kCE == 32)
         a_sraw[slot][i] = *reinterpret_cast<const uint16_t*>(a_sp[i] + (int64_t)kt * (kBK / 16));
       else
         a_sraw[slot][i] = a_sp[i][(int64_t)kt * (kBK / 16)];
@@ -343,6 +378,12 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
       if (!a_on[i]) continue;
       if constexpr (kW16) {
         *reinterpret_cast<u32x4*>(base + a_lds[i]) = a_raw[slot][i];
+        continue;
+      }
+      if constexpr (kMX) {
+        uint8_t* bb = reinterpret_cast<uint8_t*>(smem) + buf * kMxBuf;
+        *reinterpret_cast<u32x4*>(bb + a_lds[i]) = a_raw[slot][i];
+        bb[a_lds_s[i]] = (uint8_t)a_sraw[slot][i];
         continue;
       }
       const half2_t sp = scales_f16<false>(a_sraw[slot][i]);
@@ -365,17 +406,65 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
 #pragma unroll
       for (int v = 0; v < kVec; ++v)
         b_raw[buf][j][v] = *reinterpret_cast<const u32x4*>(cbase + 1024 * v);
-      const uint8_t* sp = b_sp[j] + (int64_t)kt * (64 * (kBK / 32));
-      if constexpr (kBK == 128) b_sraw[buf][j] = *reinterpret_cast<const uint32_t*>(sp);
-      else b_sraw[buf][j] = *reinterpret_cast<const uint16_t*>(sp);
+      if constexpr (kMX) {
+        const uint8_t* sp = b_sp[j] + (int64_t)kt * (64 * (kBK / 64));
+        if constexpr (kBK == 128) b_sraw[buf][j] = *reinterpret_cast<const uint16_t*>(sp);
+        else b_sraw[buf][j] = *sp;
+      } else {
+        const uint8_t* sp = b_sp[j] + (int64_t)kt * (64 * (kBK / 32));
+        if constexpr (kBK == 128) b_sraw[buf][j] = *reinterpret_cast<const uint32_t*>(sp);
+        else b_sraw[buf][j] = *reinterpret_cast<const uint16_t*>(sp);
+      }
     }
   };
   // One K step: kSteps MFMA rounds of (kMBa x 2) 32x32x16 products on LDS
   // buffer `lbuf` and B ring slot `buf`.  The operands of round s+1 (B
   // dequantised from registers, A read from LDS) are produced while round
   // s's MFMAs run.
+  // UE8M0 mode: kBK/64 rounds of (kMBa x 2) scaled 32x32x64 FP4 products.
+  // Lane (row r = lane & 31, group g) supplies, for round st, the 32 codes
+  // of its K block g * kBK/64 + st and that block's scale byte (operand
+  // select st picks it from the lane's scale register).
+  auto compute_mx = [&](int lbuf, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const uint8_t* lb = reinterpret_cast<const uint8_t*>(smem) + lbuf * kMxBuf;
+    const uint8_t* acod = lb + (lane & 31) * kLdAb + 16 * (kBK / 64) * g;
+    const uint8_t* asc = lb + kScOff + (lane & 31) * (kBK / 32) + (kBK / 64) * g;
+    int sa[kMBa];
+#pragma unroll
+    for (int i = 0; i < kMBa; ++i)
+      sa[i] = kBK == 128 ? *reinterpret_cast<const uint16_t*>(asc + i * 32 * (kBK / 32))
+                         : asc[i * 32 * (kBK / 32)];
+    auto round = [&](auto stc) {
+      constexpr int st = decltype(stc)::value;
+      i32x8_t bo[2], ao[kMBa];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 v = b_raw[buf][j][st];
+        bo[j] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int i = 0; i < kMBa; ++i) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(acod + i * 32 * kLdAb + 16 * st);
+        ao[i] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int i = 0; i < kMBa; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              ao[i], bo[j], acc[i][j], 4, 4, st, sa[i], st, (int)b_sraw[buf][j]);
+    };
+    round(Int<0>{});
+    if constexpr (kBK == 128) round(Int<1>{});
+    static_assert(kBK == 64 || kBK == 128, "one or two scaled rounds per K step");
+  };
   auto compute = [&](int lbuf, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
+    if constexpr (kMX) {
+      compute_mx(lbuf, bufc);
+      return;
+    }
     const _Float16* abase = smem + lbuf * (kBM * kLdA) + (lane & 31) * kLdA + (kBK / 2) * g;
     // block scales of this step: kBK/32 per block, as fp16 pairs
     // (8-value piece st of the lane's K range lies in block scale st / 2)
@@ -581,6 +670,31 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
           *reinterpret_cast<u32x4*>(prm.h_out + (int64_t)(row0 + row) * I + hcol) =
               *reinterpret_cast<const u32x4*>(sh + row * kLdh + 8 * pc);
       }
+    } else if constexpr (kMX) {
+      // requantise in the UE8M0 mode: rows x (kHW / 32) blocks of 32 columns
+      constexpr int kItems = 32 * kMBa * (kHW / 32);
+      const float gs = prm.out_gscale[e];
+      const int64_t ob2 = I / 2, ob32 = I / 32;
+      for (int item = tid; item < kItems; item += kThreads) {
+        const int row = item / (kHW / 32), blk = item % (kHW / 32);
+        const int32_t hcol = hbase + 32 * blk;
+        if (row < rows && hcol < I) {
+          const u32x4* src = reinterpret_cast<const u32x4*>(sh + row * kLdh + 32 * blk);
+          float xv[32];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) unpack_bf16x8(src[q], xv + 8 * q);
+          const float am = fmaxf(absmax16(xv), absmax16(xv + 16));
+          const BlockScale bsc = block_scale_ue8m0(am / kE2M1Max, gs);
+          u32x4 wv;
+          wv.x = encode8(xv, bsc.inv);
+          wv.y = encode8(xv + 8, bsc.inv);
+          wv.z = encode8(xv + 16, bsc.inv);
+          wv.w = encode8(xv + 24, bsc.inv);
+          const int64_t p = row0 + row;
+          *reinterpret_cast<u32x4*>(prm.out_codes + p * ob2 + hcol / 2) = wv;
+          prm.out_sf[p * ob32 + hcol / 32] = (uint8_t)bsc.sf;
+        }
+      }
     } else {
     // requantise: rows x (kHW / 16) blocks of 16 columns
     constexpr int kItems = 32 * kMBa * (kHW / 16);
@@ -639,7 +753,7 @@ struct Residency {
   int cus = 0, per_cu = 0;
 };
 
-template <int kWaves, int kMB, int kBK, bool kGated, int kRing, int kOcc, bool kW16>
+template <int kWaves, int kMB, int kBK, bool kGated, int kRing, int kOcc, int kMode>
 hipError_t launch(GemmParams prm, int32_t P, hipStream_t stream) {
   constexpr int kBM = 32 * kMB;
   static Residency res;
@@ -649,7 +763,7 @@ hipError_t launch(GemmParams prm, int32_t P, hipStream_t stream) {
     if (err == hipSuccess) err = hipDeviceGetAttribute(&res.cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (err == hipSuccess)
       err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &res.per_cu, (const void*)grouped_gemm_kernel<kWaves, kMB, kBK, kGated, kRing, kOcc, kW16>,
+          &res.per_cu, (const void*)grouped_gemm_kernel<kWaves, kMB, kBK, kGated, kRing, kOcc, kMode>,
           64 * kWaves, 0);
     if (err != hipSuccess) return err;
     if (res.per_cu < 1) res.per_cu = 1;
@@ -658,7 +772,7 @@ hipError_t launch(GemmParams prm, int32_t P, hipStream_t stream) {
   const int64_t slots = (int64_t)res.cus * res.per_cu;
   int64_t grid = tiles < slots ? tiles : slots;
   grid = (grid + kXcds - 1) / kXcds * kXcds;            // whole XCD rounds
-  hipLaunchKernelGGL((grouped_gemm_kernel<kWaves, kMB, kBK, kGated, kRing, kOcc, kW16>), dim3((uint32_t)grid),
+  hipLaunchKernelGGL((grouped_gemm_kernel<kWaves, kMB, kBK, kGated, kRing, kOcc, kMode>), dim3((uint32_t)grid),
                      dim3(64 * kWaves), 0, stream, prm);
   return hipGetLastError();
 }
@@ -678,15 +792,22 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream) {
   prm.E = a.E; prm.K = a.H; prm.N_w = 2 * a.I; prm.I = a.I;
   prm.out_gscale = a.out_gscale; prm.out_codes = a.out_codes; prm.out_sf = a.out_sf;
   prm.c1_dbg = a.c1_dbg; prm.h_dbg = a.h_dbg;
+  const int mode = a.mx ? kModeMX : a.w16 ? kModeW16 : kModeNV;
   if (a.P >= 32 * a.E) {
     prm.n_tiles = (a.I + 32 * kG1Waves - 1) / (32 * kG1Waves);
-    if (a.w16) return launch<kG1Waves, kG1MB, kG1BK, true, kG1Ring, kG1Occ, true>(prm, a.P, stream);
-    return launch<kG1Waves, kG1MB, kG1BK, true, kG1Ring, kG1Occ, false>(prm, a.P, stream);
+#define NVFP4_G1(m) return launch<kG1Waves, kG1MB, kG1BK, true, kG1Ring, kG1Occ, m>(prm, a.P, stream)
+    if (mode == kModeMX) NVFP4_G1(kModeMX);
+    if (mode == kModeW16) NVFP4_G1(kModeW16);
+    NVFP4_G1(kModeNV);
+#undef NVFP4_G1
   }
   constexpr int kWaves = 4;
   prm.n_tiles = (a.I + 32 * kWaves - 1) / (32 * kWaves);
-  if (a.w16) return launch<kWaves, 1, kG1BK, true, 3, 2, true>(prm, a.P, stream);
-  return launch<kWaves, 1, kG1BK, true, 3, 2, false>(prm, a.P, stream);
+#define NVFP4_G1(m) return launch<kWaves, 1, kG1BK, true, 3, 2, m>(prm, a.P, stream)
+  if (mode == kModeMX) NVFP4_G1(kModeMX);
+  if (mode == kModeW16) NVFP4_G1(kModeW16);
+  NVFP4_G1(kModeNV);
+#undef NVFP4_G1
 }
 
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream) {
@@ -699,12 +820,19 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream) {
   prm.c_out = a.out; prm.ldc = a.H;
   constexpr int kWaves = 4;
   prm.n_tiles = (a.H + 64 * kWaves - 1) / (64 * kWaves);
+  const int mode = a.mx ? kModeMX : a.w16 ? kModeW16 : kModeNV;
   if (a.P >= 32 * a.E) {
-    if (a.w16) return launch<kWaves, kG2MB, 64, false, kG2Ring, kG2Occ, true>(prm, a.P, stream);
-    return launch<kWaves, kG2MB, 64, false, kG2Ring, kG2Occ, false>(prm, a.P, stream);
+#define NVFP4_G2(m) return launch<kWaves, kG2MB, 64, false, kG2Ring, kG2Occ, m>(prm, a.P, stream)
+    if (mode == kModeMX) NVFP4_G2(kModeMX);
+    if (mode == kModeW16) NVFP4_G2(kModeW16);
+    NVFP4_G2(kModeNV);
+#undef NVFP4_G2
   }
-  if (a.w16) return launch<kWaves, 1, 64, false, 3, 2, true>(prm, a.P, stream);
-  return launch<kWaves, 1, 64, false, 3, 2, false>(prm, a.P, stream);
+#define NVFP4_G2(m) return launch<kWaves, 1, 64, false, 3, 2, m>(prm, a.P, stream)
+  if (mode == kModeMX) NVFP4_G2(kModeMX);
+  if (mode == kModeW16) NVFP4_G2(kModeW16);
+  NVFP4_G2(kModeNV);
+#undef NVFP4_G2
 }
 
 // ---- load-time weight layout conversion -----------------------------------
@@ -713,7 +841,8 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream) {
 // ks (kBK wide), the codes are stored lane by lane as the wavefront reads
 // them: piece (v, lane) = 16 bytes of row nb*32 + (lane & 31), elements
 // ks*kBK + (lane >> 5)*kBK/2 + 32v + [0, 32); the scales likewise hold, for
-// each lane, the kBK/32 block scales of that row and K range.
+// each lane, the block scales of that row and K range (kBK/32 E4M3 scales,
+// or kBK/64 UE8M0 scales in the 32-element-block mode).
 __global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t* __restrict__ src,
                                                          uint8_t* __restrict__ dst, int64_t pieces,
                                                          int32_t N, int32_t K, int32_t bk) {
@@ -736,10 +865,12 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t* __restri
 
 __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restrict__ src,
                                                           uint8_t* __restrict__ dst, int64_t items,
-                                                          int32_t N, int32_t K, int32_t bk) {
+                                                          int32_t N, int32_t K, int32_t bk,
+                                                          int32_t blk_elems) {
   const int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gi >= items) return;
-  const int32_t nks = K / bk, nb_per = N / 32, per = bk / 32;
+  // per lane: the scales of the lane's bk/2 elements (blocks of blk_elems)
+  const int32_t nks = K / bk, nb_per = N / 32, per = bk / 2 / blk_elems;
   const int32_t lane = (int32_t)(gi % 64);
   int64_t t = gi / 64;
   const int32_t ks = (int32_t)(t % nks);
@@ -747,15 +878,15 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restr
   const int32_t nb = (int32_t)(t % nb_per);
   const int64_t e = t / nb_per;
   const int64_t row = e * N + nb * 32 + (lane & 31);
-  const int64_t blk = ((int64_t)ks * bk + (lane >> 5) * (bk / 2)) / 16;
-  for (int32_t i = 0; i < per; ++i) dst[gi * per + i] = src[row * (K / 16) + blk + i];
+  const int64_t blk = ((int64_t)ks * bk + (lane >> 5) * (bk / 2)) / blk_elems;
+  for (int32_t i = 0; i < per; ++i) dst[gi * per + i] = src[row * (K / blk_elems) + blk + i];
 }
 
 int32_t weight_step_k(int32_t projection) { return projection == 0 ? kG1BK : 64; }
 
 hipError_t launch_pack_weights(int32_t projection, const uint8_t* codes, const uint8_t* sf,
                                int32_t E, int32_t N, int32_t K, uint8_t* codes_out,
-                               uint8_t* sf_out, hipStream_t stream) {
+                               uint8_t* sf_out, hipStream_t stream, bool mx) {
   const int32_t bk = weight_step_k(projection);
   const int64_t pieces = (int64_t)E * N * K / 32;        // 16-byte pieces
   const int64_t items = (int64_t)E * (N / 32) * (K / bk) * 64;
@@ -765,7 +896,7 @@ hipError_t launch_pack_weights(int32_t projection, const uint8_t* codes, const u
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(pack_scales_kernel, dim3((uint32_t)((items + 255) / 256)), dim3(256), 0,
-                     stream, sf, sf_out, items, N, K, bk);
+                     stream, sf, sf_out, items, N, K, bk, mx ? 32 : 16);
   return hipGetLastError();
 }
 

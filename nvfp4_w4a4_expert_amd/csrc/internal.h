@@ -11,7 +11,8 @@ namespace nvfp4 {
 hipError_t launch_quantize(const uint16_t* x, int64_t ldx, int32_t num_rows, int32_t K,
                            int32_t topk, const int32_t* expert_idx, const int32_t* dst_row,
                            int32_t num_experts, const float* gscale, uint8_t* codes, uint8_t* sf,
-                           int32_t num_dst_rows, hipStream_t stream, bool fp16_input = false);
+                           int32_t num_dst_rows, hipStream_t stream, bool fp16_input = false,
+                           bool mx = false);
 
 hipError_t launch_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* ids,
                         float* weights, hipStream_t stream);
@@ -39,6 +40,7 @@ struct Gemm1Args {
   int32_t a_src_div = 1;
   uint16_t* h_out = nullptr;  // [P, I] bf16 h (w16)
   bool w16 = false;
+  bool mx = false;          // UE8M0 operands: a_sf [P, H/32], w_sf 32-element blocks, out_sf [P, I/32]
   const uint8_t* w_codes;   // [E, 2I, H/2]
   const uint8_t* w_sf;      // [E, 2I, H/16]
   const float* in_scale;    // [E] w13_input_scale
@@ -57,6 +59,7 @@ struct Gemm2Args {
   const uint8_t* a_sf;      // [P, I/16]
   const uint16_t* a_rows = nullptr;  // w16: bf16 h [P, I]
   bool w16 = false;
+  bool mx = false;          // UE8M0 operands (32-element blocks)
   const uint8_t* w_codes;   // [E, H, I/2]
   const uint8_t* w_sf;      // [E, H, I/16]
   const float* in_scale;    // [E] w2_input_scale
@@ -69,7 +72,7 @@ struct Gemm2Args {
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream);
 hipError_t launch_pack_weights(int32_t projection, const uint8_t* codes, const uint8_t* sf,
                                int32_t E, int32_t N, int32_t K, uint8_t* codes_out,
-                               uint8_t* sf_out, hipStream_t stream);
+                               uint8_t* sf_out, hipStream_t stream, bool mx = false);
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream);
 
 hipError_t launch_combine(const float* c2, const float* w, const int32_t* inv, int32_t T,

@@ -109,6 +109,25 @@ __device__ __forceinline__ BlockScale block_scale(float amax_over_6, float gs) {
   return r;
 }
 
+// The UE8M0 (power-of-two) block scale of the MX-style mode (page 3, "NVFP4"
+// section: the quantiser template's UE8M0_SF switch; a block is 32
+// elements).  s = gs * amax/6 as in the E4M3 mode, encoded as the smallest
+// power of two >= s: code = biased exponent of s, plus one unless s is an
+// exact power of two, clamped to [1, 254] (s = 0 or an fp32 denormal gives 1;
+// +inf, NaN or s above 2^127 give 254).  The normalising multiplier is
+// fl32(gs / 2^(code - 127)), clamped to FLT_MAX, exactly as in the E4M3 mode.
+__device__ __forceinline__ BlockScale block_scale_ue8m0(float amax_over_6, float gs) {
+#pragma clang fp contract(off)
+  BlockScale r;
+  const float s = gs * amax_over_6;
+  const uint32_t u = __float_as_uint(s);
+  const uint32_t up = (u >> 23) + ((u & 0x7FFFFFu) != 0u ? 1u : 0u);
+  r.sf = up < 1u ? 1u : (up > 254u ? 254u : up);
+  const float sv = __uint_as_float(r.sf << 23);        // 2^(code - 127), a normal float
+  r.inv = fminf(gs / sv, kFltMax);
+  return r;
+}
+
 // Encode 8 consecutive elements, each multiplied by `inv` (one fp32 product,
 // no contraction), into one 32-bit word of packed codes: element i goes to
 // bits [4i, 4i+4).  The E2M1 rounding is done by the gfx950 conversion

@@ -9,14 +9,20 @@
 // E4M3 byte.  A wavefront's loads and stores are contiguous.
 // The kernel is HBM-bound: it reads each source row once and writes
 // topk * (K/2 + K/16) bytes per row.
+//
+// UE8M0 mode (kMX; the template's UE8M0_SF switch in the same excerpt): a
+// block is 32 elements, i.e. a pair of adjacent lanes, which exchange their
+// 16-element maxima; both lanes form the same power-of-two scale and the even
+// lane stores its byte.
 #include "internal.h"
 #include "nvfp4_device.h"
 
 namespace nvfp4 {
 
 // kE / kP / kG: expert_idx / dst_row / gscale are present (not null);
-// kF16: the source rows are fp16 instead of bf16 (both convert exactly to fp32).
-template <bool kE, bool kP, bool kG, bool kF16>
+// kF16: the source rows are fp16 instead of bf16 (both convert exactly to fp32);
+// kMX: UE8M0 scales per 32 elements instead of E4M3 scales per 16.
+template <bool kE, bool kP, bool kG, bool kF16, bool kMX>
 __global__ __launch_bounds__(1024) void quantize_experts_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int32_t num_rows, int32_t nblk, int32_t topk,
     const int32_t* __restrict__ expert_idx, const int32_t* __restrict__ dst_row,
@@ -43,8 +49,10 @@ __global__ __launch_bounds__(1024) void quantize_experts_kernel(
       unpack_bf16x8(v0, xv);
       unpack_bf16x8(v1, xv + 8);
     }
-    a6 = absmax16(xv) / kE2M1Max;
+    a6 = absmax16(xv);
   }
+  if constexpr (kMX) a6 = fmaxf(a6, __shfl_xor(a6, 1, 64));   // the block's other half
+  a6 = a6 / kE2M1Max;
 
   const int64_t row_bytes = (int64_t)nblk * 8;
   // Destinations in batches of 8 (scalar loads shared by the wavefront): the
@@ -73,53 +81,73 @@ __global__ __launch_bounds__(1024) void quantize_experts_kernel(
       if (j0 + jj >= topk || (uint32_t)p >= (uint32_t)num_dst_rows ||
           (uint32_t)e >= (uint32_t)num_experts || !on)
         continue;
-      const BlockScale bs = block_scale(a6, gb[jj]);
+      const BlockScale bs = kMX ? block_scale_ue8m0(a6, gb[jj]) : block_scale(a6, gb[jj]);
       uint2 w;
       w.x = encode8(xv, bs.inv);
       w.y = encode8(xv + 8, bs.inv);
       *reinterpret_cast<uint2*>(codes + (int64_t)p * row_bytes + (int64_t)b * 8) = w;
-      sf[(int64_t)p * nblk + b] = (uint8_t)bs.sf;
+      if constexpr (kMX) {
+        if ((b & 1) == 0) sf[(int64_t)p * (nblk / 2) + b / 2] = (uint8_t)bs.sf;
+      } else {
+        sf[(int64_t)p * nblk + b] = (uint8_t)bs.sf;
+      }
     }
   }
 }
 
+namespace {
+
+template <bool kF16, bool kMX>
+void launch_quantize_variant(int variant, dim3 grid, int32_t threads, hipStream_t stream,
+                             const uint16_t* x, int64_t ldx, int32_t num_rows, int32_t nblk,
+                             int32_t topk, const int32_t* expert_idx, const int32_t* dst_row,
+                             int32_t num_experts, const float* gscale, uint8_t* codes,
+                             uint8_t* sf, int32_t num_dst_rows) {
+#define NVFP4_QUANT_CASE(v, ke, kp, kg)                                                         \
+  case v:                                                                                       \
+    hipLaunchKernelGGL((quantize_experts_kernel<ke, kp, kg, kF16, kMX>), grid, dim3(threads),   \
+                       0, stream, x, ldx, num_rows, nblk, topk, expert_idx, dst_row,           \
+                       num_experts, gscale, codes, sf, num_dst_rows);                           \
+    break;
+  switch (variant) {
+    NVFP4_QUANT_CASE(0, false, false, false)
+    NVFP4_QUANT_CASE(1, false, false, true)
+    NVFP4_QUANT_CASE(2, false, true, false)
+    NVFP4_QUANT_CASE(3, false, true, true)
+    NVFP4_QUANT_CASE(4, true, false, false)
+    NVFP4_QUANT_CASE(5, true, false, true)
+    NVFP4_QUANT_CASE(6, true, true, false)
+    NVFP4_QUANT_CASE(7, true, true, true)
+  }
+#undef NVFP4_QUANT_CASE
+}
+
+}  // namespace
+
 hipError_t launch_quantize(const uint16_t* x, int64_t ldx, int32_t num_rows, int32_t K,
                            int32_t topk, const int32_t* expert_idx, const int32_t* dst_row,
                            int32_t num_experts, const float* gscale, uint8_t* codes, uint8_t* sf,
-                           int32_t num_dst_rows, hipStream_t stream, bool fp16_input) {
+                           int32_t num_dst_rows, hipStream_t stream, bool fp16_input, bool mx) {
   const int32_t nblk = K / 16;
   if ((int64_t)num_rows * nblk == 0) return hipSuccess;
   // 64-lane wavefronts covering the row's blocks, at most 1024 threads per
-  // workgroup (longer rows take several workgroups)
+  // workgroup (longer rows take several workgroups; 1024 is even, so the two
+  // halves of a 32-element block always share a wavefront)
   const int32_t threads = min(1024, (nblk + 63) / 64 * 64);
   const dim3 grid((uint32_t)num_rows, (uint32_t)((nblk + threads - 1) / threads));
-  const int variant = (fp16_input ? 8 : 0) | (expert_idx ? 4 : 0) | (dst_row ? 2 : 0) |
-                      (gscale ? 1 : 0);
-#define NVFP4_QUANT_CASE(v, ke, kp, kg, kf)                                                     \
-  case v:                                                                                       \
-    hipLaunchKernelGGL((quantize_experts_kernel<ke, kp, kg, kf>), grid, dim3(threads), 0,       \
-                       stream, x, ldx, num_rows, nblk, topk, expert_idx, dst_row, num_experts,  \
-                       gscale, codes, sf, num_dst_rows);                                        \
-    break;
-  switch (variant) {
-    NVFP4_QUANT_CASE(0, false, false, false, false)
-    NVFP4_QUANT_CASE(1, false, false, true, false)
-    NVFP4_QUANT_CASE(2, false, true, false, false)
-    NVFP4_QUANT_CASE(3, false, true, true, false)
-    NVFP4_QUANT_CASE(4, true, false, false, false)
-    NVFP4_QUANT_CASE(5, true, false, true, false)
-    NVFP4_QUANT_CASE(6, true, true, false, false)
-    NVFP4_QUANT_CASE(7, true, true, true, false)
-    NVFP4_QUANT_CASE(8, false, false, false, true)
-    NVFP4_QUANT_CASE(9, false, false, true, true)
-    NVFP4_QUANT_CASE(10, false, true, false, true)
-    NVFP4_QUANT_CASE(11, false, true, true, true)
-    NVFP4_QUANT_CASE(12, true, false, false, true)
-    NVFP4_QUANT_CASE(13, true, false, true, true)
-    NVFP4_QUANT_CASE(14, true, true, false, true)
-    NVFP4_QUANT_CASE(15, true, true, true, true)
-  }
-#undef NVFP4_QUANT_CASE
+  const int variant = (expert_idx ? 4 : 0) | (dst_row ? 2 : 0) | (gscale ? 1 : 0);
+  if (mx)
+    launch_quantize_variant<false, true>(variant, grid, threads, stream, x, ldx, num_rows, nblk,
+                                         topk, expert_idx, dst_row, num_experts, gscale, codes,
+                                         sf, num_dst_rows);
+  else if (fp16_input)
+    launch_quantize_variant<true, false>(variant, grid, threads, stream, x, ldx, num_rows, nblk,
+                                         topk, expert_idx, dst_row, num_experts, gscale, codes,
+                                         sf, num_dst_rows);
+  else
+    launch_quantize_variant<false, false>(variant, grid, threads, stream, x, ldx, num_rows, nblk,
+                                          topk, expert_idx, dst_row, num_experts, gscale, codes,
+                                          sf, num_dst_rows);
   return hipGetLastError();
 }
 

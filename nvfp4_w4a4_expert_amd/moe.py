@@ -91,8 +91,8 @@ class NVFP4MoELayer:
         # load-time layout conversion into the grouped GEMMs' kernel layout
         self.w13, self.w13_sf = torch.empty_like(w13), torch.empty_like(w13_sf)
         self.w2, self.w2_sf = torch.empty_like(w2), torch.empty_like(w2_sf)
-        _lib.moe_pack_weights(0, w13, w13_sf, self.E, self.H, self.I, self.w13, self.w13_sf)
-        _lib.moe_pack_weights(1, w2, w2_sf, self.E, self.H, self.I, self.w2, self.w2_sf)
+        self._pack(0, w13, w13_sf, self.E, self.H, self.I, self.w13, self.w13_sf)
+        self._pack(1, w2, w2_sf, self.E, self.H, self.I, self.w2, self.w2_sf)
         self.w13_scale2, self.w2_scale2 = up32(w13_scale2), up32(w2_scale2)
         self.device = device
         self._ws = None
@@ -108,6 +108,8 @@ class NVFP4MoELayer:
 
     _workspace_size = staticmethod(_lib.moe_workspace_size)
     _forward = staticmethod(_lib.moe_forward)
+    _pack = staticmethod(_lib.moe_pack_weights)
+    _sf_block = 16                  # elements per block scale
     _debug_names = ("topk_ids", "topk_weights", "expert_offsets", "src_pair", "inv_pair",
                     "a1_codes", "a1_sf", "c1", "h", "a2_codes", "a2_sf", "c2")
 
@@ -136,14 +138,26 @@ class NVFP4MoELayer:
                 topk_ids=((T, k), torch.int32), topk_weights=((T, k), torch.float32),
                 expert_offsets=((E + 1,), torch.int32), src_pair=((P,), torch.int32),
                 inv_pair=((P,), torch.int32), a1_codes=((P, H // 2), torch.uint8),
-                a1_sf=((P, H // 16), torch.uint8), c1=((P, 2 * I), torch.float32),
+                a1_sf=((P, H // self._sf_block), torch.uint8), c1=((P, 2 * I), torch.float32),
                 h=((P, I), torch.int16), a2_codes=((P, I // 2), torch.uint8),
-                a2_sf=((P, I // 16), torch.uint8), c2=((P, H), torch.float32))
+                a2_sf=((P, I // self._sf_block), torch.uint8), c2=((P, H), torch.float32))
             bufs = {name: torch.empty(shapes[name][0], dtype=shapes[name][1], device=dev)
                     for name in self._debug_names}
             dbg = _lib.MoEDebug(**{name: t.data_ptr() for name, t in bufs.items()})
         self._forward(w, x, logits, T, k, residual, out, ws, ws.numel(), dbg, stream)
         return (out, bufs) if debug else out
+
+
+class NVFP4MXMoELayer(NVFP4MoELayer):
+    """The W4A4 layer with UE8M0 (power-of-two) block scales per 32 elements
+    (page 3, "NVFP4" section: the quantiser template's UE8M0_SF switch).
+    Same arguments as NVFP4MoELayer, with w13_sf [E, 2I, H/32] and w2_sf
+    [E, H, I/32] UE8M0 codes (quantize_expert_weights(..., mx=True)); both
+    grouped GEMMs run on the scaled FP4 matrix instruction."""
+
+    _forward = staticmethod(_lib.moe_forward_mx)
+    _pack = staticmethod(_lib.moe_pack_weights_mx)
+    _sf_block = 32
 
 
 class NVFP4W4A16MoELayer(NVFP4MoELayer):
@@ -179,10 +193,11 @@ class NVFP4W4A16MoELayer(NVFP4MoELayer):
 
 # --- producing a layer with the library's kernels ----------------------------
 
-def quantize_expert_weights(w: torch.Tensor, stream=None):
+def quantize_expert_weights(w: torch.Tensor, stream=None, mx: bool = False):
     """Static NVFP4 quantisation of bf16 expert weights [E, N, K] on the GPU:
     weight_scale_2[e] = fl32(max|W[e]| / 2688), SFScaleVal = fl32(1 / that),
-    then the per-expert quantiser.  Returns (codes, sf, scale2) tensors."""
+    then the per-expert quantiser (UE8M0 scales per 32 elements when mx).
+    Returns (codes, sf, scale2) tensors."""
     E, N, K = (int(s) for s in w.shape)
     dev = w.device
     flat = w.reshape(E * N, K)
@@ -195,9 +210,10 @@ def quantize_expert_weights(w: torch.Tensor, stream=None):
         raise BadScaleError("weight_scale_2", slots)
     expert_of_row = torch.arange(E, dtype=torch.int32, device=dev).repeat_interleave(N)
     codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev)
-    sf = torch.empty((E, N, K // 16), dtype=torch.uint8, device=dev)
-    _lib.quantize_experts(flat, K, E * N, K, 1, expert_of_row, None, E,
-                          torch.from_numpy(gs).to(dev), codes, sf, E * N, stream)
+    sf = torch.empty((E, N, K // (32 if mx else 16)), dtype=torch.uint8, device=dev)
+    quant = _lib.quantize_experts_mx if mx else _lib.quantize_experts
+    quant(flat, K, E * N, K, 1, expert_of_row, None, E, torch.from_numpy(gs).to(dev), codes, sf,
+          E * N, stream)
     return codes, sf, torch.from_numpy(scale2).to(dev)
 
 
@@ -210,13 +226,14 @@ class Calibration:
 
 
 def calibrate_layer(w13c, w13s, w13s2, w2c, w2s, w2s2, x_cal: torch.Tensor,
-                    logits_cal: torch.Tensor, k: int) -> Calibration:
+                    logits_cal: torch.Tensor, k: int, mx: bool = False) -> Calibration:
     """Per-expert activation scales from a calibration batch, with the
     library's calibration pass (nvfp4_calibrate_input_scales):
     w13_input_scale = fl32(amax|x| / 2688) over the rows routed to each
     expert; w2_input_scale = fl32(amax|h| / 2688) over the same rows, where h
     is the layer's own SiLU(gate)*up (which does not depend on the a2 scale).
-    Experts without calibration rows stay unwritten (NaN, written 0)."""
+    Experts without calibration rows stay unwritten (NaN, written 0).  mx:
+    the weights are in the UE8M0 mode and h comes from that layer."""
     dev = x_cal.device
     Tc, H = (int(s) for s in x_cal.shape)
     E = int(w13c.shape[0])
@@ -238,7 +255,8 @@ def calibrate_layer(w13c, w13s, w13s2, w2c, w2s, w2s2, x_cal: torch.Tensor,
     # a2 scales, restricted to the written slots, and read h back.
     ones = np.ones(E, dtype=np.float32)
     s13_run = np.where(written == 1, s13, np.float32(1.0)).astype(np.float32)
-    layer = NVFP4MoELayer(w13c, w13s, w13s2, w2c, w2s, w2s2, s13_run, ones, device=dev)
+    cls = NVFP4MXMoELayer if mx else NVFP4MoELayer
+    layer = cls(w13c, w13s, w13s2, w2c, w2s, w2s2, s13_run, ones, device=dev)
     _, dbg = layer.forward(x_cal, logits_cal, k, debug=True)
     s2_d = torch.empty(E, dtype=torch.float32, device=dev)
     written2_d = torch.empty(E, dtype=torch.uint8, device=dev)

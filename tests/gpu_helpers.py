@@ -14,6 +14,7 @@ import numpy as np
 import synthetic as S
 from oracle import formats as OF
 from oracle import moe as OM
+from oracle import mx as OX
 from oracle import quant as OQ
 
 # Per-row relative L2 bound for expert-GEMM outputs and the layer output,
@@ -58,6 +59,21 @@ def oracle_layer(name: str, layer: int = 0) -> OM.Layer:
     return _prepare(key_name, layer)
 
 
+@functools.lru_cache(maxsize=2)
+def oracle_layer_mx(name: str, layer: int = 0) -> OX.LayerMX:
+    """The oracle's layer in the UE8M0 mode (weights quantised and scales
+    calibrated by the oracle); decode and prefill share one layer."""
+    key_name = "decode" if name == "prefill" else name
+    w = S.WORKLOADS[key_name]
+    t0 = time.time()
+    progress(f"oracle: drawing {key_name} layer {layer} weights (UE8M0 mode)")
+    w13, w2 = S.expert_weights(w, layer=layer)
+    xc, lc = S.calibration_batch(w, layer=layer)
+    out = OX.prepare_layer(w13, w2, xc, lc, w.k, threads=16)
+    progress(f"oracle: UE8M0 {key_name} layer {layer} ready in {time.time() - t0:.1f}s")
+    return out
+
+
 @functools.lru_cache(maxsize=4)
 def _prepare(name: str, layer: int) -> OM.Layer:
     w = S.WORKLOADS[name]
@@ -82,6 +98,13 @@ def device_layer(layer: OM.Layer):
                            layer.written13, layer.written2, device="cuda")
 
 
+def device_layer_mx(layer: OX.LayerMX):
+    from nvfp4_w4a4_expert_amd import moe as M
+    return M.NVFP4MXMoELayer(layer.w13c, layer.w13s, layer.w13s2, layer.w2c, layer.w2s,
+                             layer.w2s2, layer.w13_input_scale, layer.w2_input_scale,
+                             layer.written13, layer.written2, device="cuda")
+
+
 def device_layer_w4a16(layer: OM.Layer):
     """The weight-only layer: weights only, no activation scale passed."""
     from nvfp4_w4a4_expert_amd import moe as M
@@ -89,11 +112,12 @@ def device_layer_w4a16(layer: OM.Layer):
                                 layer.w2s2, device="cuda")
 
 
-def run_forward(layer: OM.Layer, x_bits, logits, k, residual_bits=None, w4a16=False):
+def run_forward(layer: OM.Layer, x_bits, logits, k, residual_bits=None, w4a16=False, mx=False):
     """GPU forward with every intermediate dumped; returns numpy arrays."""
     import torch
     from nvfp4_w4a4_expert_amd import moe as M
-    dl = device_layer_w4a16(layer) if w4a16 else device_layer(layer)
+    dl = (device_layer_w4a16(layer) if w4a16 else device_layer_mx(layer) if mx
+          else device_layer(layer))
     x = M.bf16_tensor(x_bits)
     lg = torch.from_numpy(np.ascontiguousarray(logits, dtype=np.float32)).cuda()
     res = None if residual_bits is None else M.bf16_tensor(residual_bits)
@@ -105,8 +129,10 @@ def run_forward(layer: OM.Layer, x_bits, logits, k, residual_bits=None, w4a16=Fa
     return got
 
 
-def check_layer_parity(layer: OM.Layer, x_bits, logits, k, residual_bits=None, label=""):
-    """Stage-by-stage parity of one GPU forward against the oracle.
+def check_layer_parity(layer: OM.Layer, x_bits, logits, k, residual_bits=None, label="",
+                       mx=False):
+    """Stage-by-stage parity of one GPU forward against the oracle (of the
+    UE8M0 mode when mx, with an OX.LayerMX).
 
     Unique results are compared exactly (routing ids, permutation, A1 codes
     and scales).  Floating-point stages are compared per row within
@@ -117,9 +143,10 @@ def check_layer_parity(layer: OM.Layer, x_bits, logits, k, residual_bits=None, l
     T = x_bits.shape[0]
     E, I = layer.E, layer.I
     progress(f"{label}: GPU forward")
-    got = run_forward(layer, x_bits, logits, k, residual_bits)
+    got = run_forward(layer, x_bits, logits, k, residual_bits, mx=mx)
     progress(f"{label}: oracle forward")
-    ref = OM.layer_forward(layer, x_bits, logits, k, residual_bits)
+    OQm = OX if mx else OQ
+    ref = (OX if mx else OM).layer_forward(layer, x_bits, logits, k, residual_bits)
     progress(f"{label}: comparing")
 
     assert np.array_equal(got["topk_ids"], ref["ids"]), label + " routing ids"
@@ -141,13 +168,13 @@ def check_layer_parity(layer: OM.Layer, x_bits, logits, k, residual_bits=None, l
     hr = rel_l2_rows(h_gpu, h_exact)
 
     rexp = OM.row_experts(ref["offsets"])
-    a2c, a2s = OQ.quantize_experts(got["h"], rexp, ref["a2_gscale"])
+    a2c, a2s = OQm.quantize_experts(got["h"], rexp, ref["a2_gscale"])
     assert np.array_equal(got["a2_codes"], a2c), label + " A2 codes vs Q(h_gpu)"
     assert np.array_equal(got["a2_sf"], a2s), label + " A2 scales vs Q(h_gpu)"
 
     progress(f"{label}: oracle GEMM2 over the GPU's A2")
-    c2_ref = OM.grouped_gemm_ref(got["a2_codes"], got["a2_sf"], ref["offsets"], layer.w2c,
-                                 layer.w2s, layer.alpha2)
+    c2_ref = (OX if mx else OM).grouped_gemm_ref(got["a2_codes"], got["a2_sf"], ref["offsets"],
+                                                 layer.w2c, layer.w2s, layer.alpha2)
     c2 = rel_l2_rows(got["c2"], c2_ref)
     assert c2.max() <= REL_L2_TOL, (label, "C2", c2.max())
 

@@ -33,7 +33,9 @@ def test_header_declares_the_boundary():
                  "nvfp4_expert_absmax", "nvfp4_status_string", "nvfp4_abi_version",
                  "nvfp4_selftest_conversions", "nvfp4_moe_pack_weights",
                  "nvfp4_quantize_experts_fp16", "nvfp4_calibrate_input_scales",
-                 "nvfp4_moe_forward_w4a16", "nvfp4_moe_workspace_size_w4a16"]:
+                 "nvfp4_moe_forward_w4a16", "nvfp4_moe_workspace_size_w4a16",
+                 "nvfp4_quantize_experts_mx", "nvfp4_moe_pack_weights_mx",
+                 "nvfp4_moe_forward_mx"]:
         assert name in syms
 
 
@@ -47,7 +49,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = _lib()
-    assert L.abi_version() == 3
+    assert L.abi_version() == 4
     for s in range(6):
         assert L.status_string(s)
     assert "unknown" in L.status_string(99)
