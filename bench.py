@@ -29,6 +29,7 @@ import numpy as np
 
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E peak
 MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16/bf16 MFMA peak
+MFMA_FP4_PEAK_TFLOPS = 10100.0   # MI355X dense FP4 (scaled MFMA) peak
 
 METRIC = "NVFP4 MoE layer tokens/s (hidden 2816, 128 experts) + quantizer HBM GB/s"
 
@@ -43,7 +44,11 @@ def parse_args():
                     help="skip the decode sub-measurement of the prefill run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=64)
+    ap.add_argument("--no-w4a16", action="store_true",
+                    help="skip the weight-only (W4A16) sub-measurement")
+    ap.add_argument("--no-mx", action="store_true",
+                    help="skip the UE8M0 (MX-style) sub-measurement")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
                          "known-size reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -126,72 +131,87 @@ def measured_traffic():
         return None
 
 
-def build_layer(w, torch, M, layer=0):
+def build_layer(w, torch, M, layer=0, mx=False):
     """Seeded bf16 expert weights -> NVFP4 with the library's quantiser;
     activation scales calibrated with the library's kernels on the layer's
-    unbiased calibration batch."""
+    unbiased calibration batch (UE8M0 block scales throughout when mx)."""
     import synthetic as S
     t0 = time.time()
     w13_bits, w2_bits = S.expert_weights(w, layer=layer)
     w13 = M.bf16_tensor(w13_bits)
     w2 = M.bf16_tensor(w2_bits)
     del w13_bits, w2_bits
-    w13c, w13s, w13s2 = M.quantize_expert_weights(w13)
-    w2c, w2s, w2s2 = M.quantize_expert_weights(w2)
+    w13c, w13s, w13s2 = M.quantize_expert_weights(w13, mx=mx)
+    w2c, w2s, w2s2 = M.quantize_expert_weights(w2, mx=mx)
     del w13, w2
     xc, lc = S.calibration_batch(w, layer=layer)
     cal = M.calibrate_layer(w13c, w13s, w13s2, w2c, w2s, w2s2, M.bf16_tensor(xc),
-                            torch.from_numpy(lc).cuda(), w.k)
-    lay = M.NVFP4MoELayer(w13c, w13s, w13s2, w2c, w2s, w2s2, cal.w13_input_scale,
-                          cal.w2_input_scale, cal.written13, cal.written2)
+                            torch.from_numpy(lc).cuda(), w.k, mx=mx)
+    cls = M.NVFP4MXMoELayer if mx else M.NVFP4MoELayer
+    lay = cls(w13c, w13s, w13s2, w2c, w2s, w2s2, cal.w13_input_scale,
+              cal.w2_input_scale, cal.written13, cal.written2)
     torch.cuda.synchronize()
-    log(f"{w.name} layer {layer} prepared in {time.time() - t0:.1f}s")
+    log(f"{w.name} layer {layer}{' (UE8M0)' if mx else ''} prepared in {time.time() - t0:.1f}s")
     return lay
 
 
-def time_steps(torch, L, events, runs, steps, warmup, T, k, stage_events=True):
+def time_steps(torch, L, events, runs, steps, warmup, T, k, stage_events=True, fwd=None):
     """Time `steps` calls of nvfp4_moe_forward cycling over `runs` (list of
     (weights, workspace tensor, x, logits, out)); HIP events on torch's
-    current stream, which the library launches on.  Returns (ms per step,
-    host wall s, per-stage µs or None)."""
+    current stream, which the library launches on.  `fwd` replaces
+    nvfp4_moe_forward (the weight-only forward has the same signature).
+
+    Two timed passes over the same steps: the first, uninstrumented, gives
+    the step time; the second records HIP events before the first launch
+    and after every kernel of every step and gives the per-kernel times.
+    (An event record costs about 3.5 µs of GPU time on this stack, so
+    instrumenting the first pass would add ~20 µs to every step.)  Returns
+    (ms per step, host wall s, per-stage µs or None, instrumented ms per
+    step or None)."""
+    fwd = fwd or L.moe_forward
     stream = torch.cuda.current_stream().cuda_stream
     nst = len(L.MOE_STAGES)
-    evs = [events.create(nst + 1) for _ in range(steps)] if stage_events else None
-    dbgs = ([L.MoEDebug(stage_events=ctypes.cast(e, ctypes.POINTER(ctypes.c_void_p)))
-             for e in evs] if stage_events else None)
 
     def step(i, dbg=None):
         wst, ws, x, lg, out = runs[i % len(runs)]
-        L.moe_forward(wst, x, lg, T, k, None, out, ws, ws.numel(), dbg, stream)
+        fwd(wst, x, lg, T, k, None, out, ws, ws.numel(), dbg, stream)
+
+    def timed(dbgs):
+        torch.cuda.synchronize()
+        ev = events.create(2)
+        events.record(ev[0], stream)
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i, dbgs[i] if dbgs else None)
+        events.record(ev[1], stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = events.elapsed_ms(ev[0], ev[1]) / steps
+        events.destroy(ev)
+        return ms, wall
 
     for i in range(warmup):
         step(i)
-    torch.cuda.synchronize()
-    ev = events.create(2)
-    events.record(ev[0], stream)
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(i, dbgs[i] if stage_events else None)
-    events.record(ev[1], stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = events.elapsed_ms(ev[0], ev[1]) / steps
-    events.destroy(ev)
-    stage_us = None
-    if stage_events:
-        stage_ms = np.zeros(nst)
-        for e in evs:
-            for s_ in range(nst):
-                stage_ms[s_] += events.elapsed_ms(e[s_], e[s_ + 1])
-            events.destroy(e)
-        stage_us = {name: 1000.0 * v / steps for name, v in zip(L.MOE_STAGES, stage_ms)}
-    return ms_step, wall, stage_us
+    ms_step, wall = timed(None)
+    if not stage_events:
+        return ms_step, wall, None, None
+    evs = [events.create(nst + 1) for _ in range(steps)]
+    dbgs = [L.MoEDebug(stage_events=ctypes.cast(e, ctypes.POINTER(ctypes.c_void_p)))
+            for e in evs]
+    ms_instr, _ = timed(dbgs)
+    stage_ms = np.zeros(nst)
+    for e in evs:
+        for s_ in range(nst):
+            stage_ms[s_] += events.elapsed_ms(e[s_], e[s_ + 1])
+        events.destroy(e)
+    stage_us = {name: 1000.0 * v / steps for name, v in zip(L.MOE_STAGES, stage_ms)}
+    return ms_step, wall, stage_us, ms_instr
 
 
 def bench_layer(args, torch, M, L, events, w, layer):
-    """The layer on three rotating seeded input sets of workload w.  Every
-    timed step also records HIP events between its launches, so the
-    per-kernel times come from the timed region."""
+    """The layer on three rotating seeded input sets of workload w: the
+    step time from an uninstrumented timed pass, the per-kernel times from
+    an instrumented pass over the same steps (time_steps)."""
     import synthetic as S
     wst = layer.weights()
     ws = layer.workspace(w.T, w.k)
@@ -201,6 +221,71 @@ def bench_layer(args, torch, M, L, events, w, layer):
         lg = torch.from_numpy(S.router_logits(w, layer=i)).cuda()
         runs.append((wst, ws, x, lg, torch.empty_like(x)))
     return time_steps(torch, L, events, runs, args.steps, args.warmup, w.T, w.k)
+
+
+def bench_w4a16(args, torch, M, L, events, layers):
+    """The weight-only (W4A16) forward over the same packed weights: the
+    prefill layer (three input sets) and the 16-token decode step on two
+    alternating layers.  Same stage events (the quantise stage is empty)."""
+    import synthetic as S
+    views = [M.NVFP4W4A16MoELayer.sharing(lay) for lay in layers]
+    out = {}
+    for name, steps, lays in (("prefill", args.steps, views[:1]),
+                              ("decode", max(args.steps, 200), views)):
+        w = S.WORKLOADS[name]
+        runs = []
+        for i in range(3):
+            x = M.bf16_tensor(S.activations(w, layer=i))
+            lg = torch.from_numpy(S.router_logits(w, layer=i)).cuda()
+            for v in lays:
+                runs.append((v.weights(), v.workspace(w.T, w.k), x, lg, torch.empty_like(x)))
+        ms, _, st, ms_i = time_steps(torch, L, events, runs, steps, args.warmup, w.T, w.k,
+                               fwd=L.moe_forward_w4a16)
+        P = w.T * w.k
+        f1 = 2.0 * P * (2 * w.I) * w.H
+        f2 = 2.0 * P * w.H * w.I
+        g1, g2 = st["gemm1_w13"], st["gemm2_w2"]
+        out[name] = dict(tokens_per_s=round(w.T / (ms * 1e-3), 1), us_per_step=round(ms * 1000, 2),
+                         us_per_step_instrumented=round(ms_i * 1000, 2),
+                         stages_us={k_: round(v, 2) for k_, v in st.items()},
+                         gemm1_tflops=round(f1 / (g1 * 1e-6) / 1e12, 1),
+                         gemm2_tflops=round(f2 / (g2 * 1e-6) / 1e12, 1),
+                         gemm1_frac_of_bf16_peak=round(f1 / (g1 * 1e-6) / 1e12
+                                                       / MFMA_F16_PEAK_TFLOPS, 4))
+    return out
+
+
+def bench_mx(args, torch, M, L, events):
+    """The UE8M0 (MX-style) mode: its own layers (weights quantised with
+    UE8M0 scales, activation scales calibrated through that mode), the
+    prefill layer and the 16-token decode step on two alternating layers.
+    GEMM rates against the dense FP4 matrix peak."""
+    import synthetic as S
+    layers = [build_layer(S.WORKLOADS["decode"], torch, M, layer=i, mx=True) for i in range(2)]
+    out = {}
+    for name, steps, lays in (("prefill", args.steps, layers[:1]),
+                              ("decode", max(args.steps, 200), layers)):
+        w = S.WORKLOADS[name]
+        runs = []
+        for i in range(3):
+            x = M.bf16_tensor(S.activations(w, layer=i))
+            lg = torch.from_numpy(S.router_logits(w, layer=i)).cuda()
+            for v in lays:
+                runs.append((v.weights(), v.workspace(w.T, w.k), x, lg, torch.empty_like(x)))
+        ms, _, st, ms_i = time_steps(torch, L, events, runs, steps, args.warmup, w.T, w.k,
+                                     fwd=L.moe_forward_mx)
+        P = w.T * w.k
+        f1 = 2.0 * P * (2 * w.I) * w.H
+        f2 = 2.0 * P * w.H * w.I
+        g1, g2 = st["gemm1_w13"], st["gemm2_w2"]
+        out[name] = dict(tokens_per_s=round(w.T / (ms * 1e-3), 1), us_per_step=round(ms * 1000, 2),
+                         us_per_step_instrumented=round(ms_i * 1000, 2),
+                         stages_us={k_: round(v, 2) for k_, v in st.items()},
+                         gemm1_tflops=round(f1 / (g1 * 1e-6) / 1e12, 1),
+                         gemm2_tflops=round(f2 / (g2 * 1e-6) / 1e12, 1),
+                         gemm1_frac_of_fp4_peak=round(f1 / (g1 * 1e-6) / 1e12
+                                                      / MFMA_FP4_PEAK_TFLOPS, 4))
+    return out
 
 
 def bench_decode(args, torch, M, L, events, layers):
@@ -222,7 +307,7 @@ def bench_decode(args, torch, M, L, events, layers):
     order = [runs[li * 3 + i] for i in range(3) for li in range(len(layers))]
     hit_order = [hits[li * 3 + i] for i in range(3) for li in range(len(layers))]
     steps = max(args.steps, 200)
-    ms, wall, st = time_steps(torch, L, events, order, steps, args.warmup, w.T, w.k)
+    ms, wall, st, ms_i = time_steps(torch, L, events, order, steps, args.warmup, w.T, w.k)
     n_hit = float(np.mean(hit_order))
     per_expert = 2 * w.I * w.H * 9 // 16 + w.H * w.I * 9 // 16       # w13 + w2 codes+scales
     g1_bytes = n_hit * (2 * w.I * w.H * 9 // 16)
@@ -230,7 +315,7 @@ def bench_decode(args, torch, M, L, events, layers):
     return dict(workload=f"decode MoE layer: {w.T} tokens, hidden {w.H}, {w.E} experts, "
                          f"intermediate {w.I}, top-{w.k}; 2 alternating layers x 3 input sets",
                 tokens_per_s=round(w.T / (ms * 1e-3), 1), us_per_step=round(ms * 1000, 2),
-                experts_hit=round(n_hit, 1),
+                us_per_step_instrumented=round(ms_i * 1000, 2), experts_hit=round(n_hit, 1),
                 weight_bytes_per_step=int(n_hit * per_expert),
                 layer_weight_gbps=round(n_hit * per_expert / (ms * 1e-3) / 1e9, 1),
                 gemm1_weight_gbps=round(g1_bytes / (g1 * 1e-6) / 1e9, 1),
@@ -412,7 +497,7 @@ def main():
     events = HipEvents()
 
     import synthetic as S
-    decode = copy_gbps = quant = cpu = None
+    decode = copy_gbps = quant = cpu = w4a16 = mx = ms_instr = None
     if args.workload == "stack":
         w, st = bench_stack(args, torch, M, L, events)
         ms_step, wall, stage_us = st["ms_per_stack"], None, None
@@ -429,7 +514,7 @@ def main():
         layer = build_layer(S.WORKLOADS["decode"], torch, M)
         if args.workload == "prefill":
             w = S.WORKLOADS["prefill"]
-            ms_step, wall, stage_us = bench_layer(args, torch, M, L, events, w, layer)
+            ms_step, wall, stage_us, ms_instr = bench_layer(args, torch, M, L, events, w, layer)
             tokens_per_s = w.T / (ms_step * 1e-3)
             log(f"layer: {ms_step * 1000:.1f} us/step, {tokens_per_s:.4g} tokens/s; "
                 f"stages {stage_us}")
@@ -447,17 +532,25 @@ def main():
             tf = (flops_gemm1 + flops_gemm2) / (gemm_us * 1e-6) / 1e12
             gemms = dict(us=round(gemm_us, 2), tflops=round(tf, 1),
                          frac_of_f16_peak=round(tf / MFMA_F16_PEAK_TFLOPS, 4))
-            if not args.no_decode:
+            if not args.no_decode or not args.no_w4a16:
                 second = build_layer(S.WORKLOADS["decode"], torch, M, layer=1)
-                decode = bench_decode(args, torch, M, L, events, [layer, second])
-                log(f"decode: {decode}")
+                if not args.no_decode:
+                    decode = bench_decode(args, torch, M, L, events, [layer, second])
+                    log(f"decode: {decode}")
+                if not args.no_w4a16:
+                    w4a16 = bench_w4a16(args, torch, M, L, events, [layer, second])
+                    log(f"w4a16: {w4a16}")
                 del second
+            if not args.no_mx:
+                mx = bench_mx(args, torch, M, L, events)
+                log(f"mx: {mx}")
         else:                                             # decode
             w = S.WORKLOADS["decode"]
             second = build_layer(w, torch, M, layer=1)
             decode = bench_decode(args, torch, M, L, events, [layer, second])
             log(f"decode: {decode}")
             ms_step, wall, stage_us = decode["us_per_step"] / 1000.0, None, decode["stages_us"]
+            ms_instr = decode["us_per_step_instrumented"] / 1000.0
             tokens_per_s = decode["tokens_per_s"]
             g1 = stage_us["gemm1_w13"]
             roofline = dict(kernel="grouped_gemm_kernel<true> (w13, weight streaming)",
@@ -466,7 +559,7 @@ def main():
                             frac=decode["gemm1_frac_of_hbm_peak"], traffic=None,
                             experts_hit=decode["experts_hit"], us_per_launch=round(g1, 2))
             gemms = None
-        extra = dict(decode=decode)
+        extra = dict(decode=decode, w4a16=w4a16, mx=mx)
         del layer
 
     if args.workload == "prefill":
@@ -487,6 +580,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_instrumented": round(ms_instr, 5) if ms_instr is not None else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -415,7 +415,8 @@ NVFP4_API nvfp4_status_t nvfp4_quantize_experts_mx(const void* x_bf16, int64_t l
 /*
  * nvfp4_moe_pack_weights_mx — nvfp4_moe_pack_weights for UE8M0 weights:
  * scales are [E, 2I, H/32] (projection 0) or [E, H, I/32] (projection 1);
- * codes as in the E4M3 mode.  Same requirements and errors.
+ * codes as in the E4M3 mode (w13 with a 256-wide K step).  Same errors;
+ * requires H % 256 == 0 and I % 64 == 0 (else NVFP4_ERR_UNSUPPORTED).
  */
 NVFP4_API nvfp4_status_t nvfp4_moe_pack_weights_mx(int32_t projection, const uint8_t* codes,
                                                    const uint8_t* sf, int32_t num_experts,
@@ -430,9 +431,9 @@ NVFP4_API nvfp4_status_t nvfp4_moe_pack_weights_mx(int32_t projection, const uin
  * SFScaleVal), both grouped GEMMs on the gfx950 scaled FP4 matrix instruction
  * (the power-of-two block scales are applied by the instruction; nothing is
  * dequantised), alpha = input_scale * weight_scale_2 as in the E4M3 mode.
- * Same arguments, requirements, workspace (nvfp4_moe_workspace_size) and
- * debug buffers as nvfp4_moe_forward; debug a1_sf / a2_sf receive [P, H/32]
- * and [P, I/32] UE8M0 codes.
+ * Same arguments, workspace (nvfp4_moe_workspace_size) and debug buffers as
+ * nvfp4_moe_forward, plus H % 256 == 0; debug a1_sf / a2_sf receive
+ * [P, H/32] and [P, I/32] UE8M0 codes.
  */
 NVFP4_API nvfp4_status_t nvfp4_moe_forward_mx(const nvfp4_moe_weights_t* w, const void* x_bf16,
                                               const float* router_logits, int32_t num_tokens,

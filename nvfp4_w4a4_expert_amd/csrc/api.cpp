@@ -242,7 +242,7 @@ nvfp4_status_t pack_weights(int32_t projection, const uint8_t* codes, const uint
   if (projection != 0 && projection != 1) return NVFP4_ERR_INVALID_ARG;
   if (num_experts < 1 || hidden <= 0 || inter <= 0 || hidden % 16 || inter % 16)
     return NVFP4_ERR_INVALID_ARG;
-  if (hidden % 128 || inter % 64) return NVFP4_ERR_UNSUPPORTED;
+  if (hidden % 128 || inter % 64 || (mx && hidden % 256)) return NVFP4_ERR_UNSUPPORTED;
   if (!codes || !sf || !codes_out || !sf_out || codes == codes_out || sf == sf_out)
     return NVFP4_ERR_INVALID_ARG;
   if (!aligned(codes, 16) || !aligned(codes_out, 16)) return NVFP4_ERR_INVALID_ARG;
@@ -308,6 +308,7 @@ nvfp4_status_t moe_forward(const nvfp4_moe_weights_t* w, const void* x_bf16,
   nvfp4_status_t st = check_weights(w, w16);
   if (st != NVFP4_OK) return st;
   const int32_t E = w->num_experts, H = w->hidden, I = w->inter;
+  if (mx && H % 256) return NVFP4_ERR_UNSUPPORTED;
   if (num_tokens < 0 || k < 1 || k > E) return NVFP4_ERR_INVALID_ARG;
   if (k > 32) return NVFP4_ERR_UNSUPPORTED;
   if ((int64_t)num_tokens * k > (1 << 30)) return NVFP4_ERR_UNSUPPORTED;

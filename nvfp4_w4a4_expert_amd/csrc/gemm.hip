@@ -100,6 +100,9 @@ constexpr int kXcds = 8;
 // tiles either do not fit with 3-slot rings or lose more to latency with
 // 2-slot rings than they save in dequantisation.)
 constexpr int kG1Waves = 8, kG1MB = 2, kG1BK = 128, kG1Ring = 3, kG1Occ = 1;
+// UE8M0 mode w13: K step 256 (nothing to dequantise, so a 128-wide step is
+// too little matrix work per barrier and per prefetch slot)
+constexpr int kG1BKmx = 256;
 constexpr int kG2MB = 4, kG2Ring = 2, kG2Occ = 2;
 constexpr int kMaxExperts = 1024;
 
@@ -408,7 +411,8 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
         b_raw[buf][j][v] = *reinterpret_cast<const u32x4*>(cbase + 1024 * v);
       if constexpr (kMX) {
         const uint8_t* sp = b_sp[j] + (int64_t)kt * (64 * (kBK / 64));
-        if constexpr (kBK == 128) b_sraw[buf][j] = *reinterpret_cast<const uint16_t*>(sp);
+        if constexpr (kBK == 256) b_sraw[buf][j] = *reinterpret_cast<const uint32_t*>(sp);
+        else if constexpr (kBK == 128) b_sraw[buf][j] = *reinterpret_cast<const uint16_t*>(sp);
         else b_sraw[buf][j] = *sp;
       } else {
         const uint8_t* sp = b_sp[j] + (int64_t)kt * (64 * (kBK / 32));
@@ -432,9 +436,11 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
     const uint8_t* asc = lb + kScOff + (lane & 31) * (kBK / 32) + (kBK / 64) * g;
     int sa[kMBa];
 #pragma unroll
-    for (int i = 0; i < kMBa; ++i)
-      sa[i] = kBK == 128 ? *reinterpret_cast<const uint16_t*>(asc + i * 32 * (kBK / 32))
-                         : asc[i * 32 * (kBK / 32)];
+    for (int i = 0; i < kMBa; ++i) {
+      const uint8_t* q = asc + i * 32 * (kBK / 32);
+      sa[i] = kBK == 256 ? (int)*reinterpret_cast<const uint32_t*>(q)
+            : kBK == 128 ? (int)*reinterpret_cast<const uint16_t*>(q) : (int)*q;
+    }
     auto round = [&](auto stc) {
       constexpr int st = decltype(stc)::value;
       i32x8_t bo[2], ao[kMBa];
@@ -455,9 +461,13 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               ao[i], bo[j], acc[i][j], 4, 4, st, sa[i], st, (int)b_sraw[buf][j]);
     };
+    static_assert(kBK == 64 || kBK == 128 || kBK == 256, "1, 2 or 4 scaled rounds per K step");
     round(Int<0>{});
-    if constexpr (kBK == 128) round(Int<1>{});
-    static_assert(kBK == 64 || kBK == 128, "one or two scaled rounds per K step");
+    if constexpr (kBK >= 128) round(Int<1>{});
+    if constexpr (kBK == 256) {
+      round(Int<2>{});
+      round(Int<3>{});
+    }
   };
   auto compute = [&](int lbuf, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
@@ -796,7 +806,8 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream) {
   if (a.P >= 32 * a.E) {
     prm.n_tiles = (a.I + 32 * kG1Waves - 1) / (32 * kG1Waves);
 #define NVFP4_G1(m) return launch<kG1Waves, kG1MB, kG1BK, true, kG1Ring, kG1Occ, m>(prm, a.P, stream)
-    if (mode == kModeMX) NVFP4_G1(kModeMX);
+    if (mode == kModeMX)
+      return launch<kG1Waves, kG1MB, kG1BKmx, true, kG1Ring, kG1Occ, kModeMX>(prm, a.P, stream);
     if (mode == kModeW16) NVFP4_G1(kModeW16);
     NVFP4_G1(kModeNV);
 #undef NVFP4_G1
@@ -804,7 +815,7 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream) {
   constexpr int kWaves = 4;
   prm.n_tiles = (a.I + 32 * kWaves - 1) / (32 * kWaves);
 #define NVFP4_G1(m) return launch<kWaves, 1, kG1BK, true, 3, 2, m>(prm, a.P, stream)
-  if (mode == kModeMX) NVFP4_G1(kModeMX);
+  if (mode == kModeMX) return launch<kWaves, 1, kG1BKmx, true, 3, 2, kModeMX>(prm, a.P, stream);
   if (mode == kModeW16) NVFP4_G1(kModeW16);
   NVFP4_G1(kModeNV);
 #undef NVFP4_G1
@@ -882,12 +893,14 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restr
   for (int32_t i = 0; i < per; ++i) dst[gi * per + i] = src[row * (K / blk_elems) + blk + i];
 }
 
-int32_t weight_step_k(int32_t projection) { return projection == 0 ? kG1BK : 64; }
+int32_t weight_step_k(int32_t projection, bool mx) {
+  return projection == 0 ? (mx ? kG1BKmx : kG1BK) : 64;
+}
 
 hipError_t launch_pack_weights(int32_t projection, const uint8_t* codes, const uint8_t* sf,
                                int32_t E, int32_t N, int32_t K, uint8_t* codes_out,
                                uint8_t* sf_out, hipStream_t stream, bool mx) {
-  const int32_t bk = weight_step_k(projection);
+  const int32_t bk = weight_step_k(projection, mx);
   const int64_t pieces = (int64_t)E * N * K / 32;        // 16-byte pieces
   const int64_t items = (int64_t)E * (N / 32) * (K / bk) * 64;
   if (pieces == 0) return hipSuccess;
