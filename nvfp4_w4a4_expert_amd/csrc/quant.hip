@@ -3,17 +3,18 @@
 //
 // Token-major: a workgroup owns one source row, one 16-element block per
 // lane.  The row, its topk destinations and their SFScaleVals are uniform
-// (scalar loads); each lane loads its block once,
-// forms amax/6 once, and for every destination applies that expert's
-// SFScaleVal, encodes 16 codes and stores 8 bytes of packed codes plus one
-// E4M3 byte.  A wavefront's loads and stores are contiguous.
+// (scalar loads); each lane loads its block once, forms amax/6 once, and for
+// every destination applies that expert's SFScaleVal, encodes 16 codes and
+// stores 8 bytes of packed codes plus its E4M3 byte.  A wavefront's loads and
+// stores are contiguous.
 // The kernel is HBM-bound: it reads each source row once and writes
 // topk * (K/2 + K/16) bytes per row.
 //
 // UE8M0 mode (kMX; the template's UE8M0_SF switch in the same excerpt): a
 // block is 32 elements, i.e. a pair of adjacent lanes, which exchange their
-// 16-element maxima; both lanes form the same power-of-two scale and the even
-// lane stores its byte.
+// 16-element maxima; both lanes form the same power-of-two scale.
+// Scale bytes leave as 32-bit words gathered across lanes when the row's
+// scale count is a multiple of 4 (byte stores otherwise).
 #include "internal.h"
 #include "nvfp4_device.h"
 
@@ -53,8 +54,10 @@ __global__ __launch_bounds__(1024) void quantize_experts_kernel(
   }
   if constexpr (kMX) a6 = fmaxf(a6, __shfl_xor(a6, 1, 64));   // the block's other half
   a6 = a6 / kE2M1Max;
-
   const int64_t row_bytes = (int64_t)nblk * 8;
+  // whole 32-bit scale words per destination row (and an aligned array):
+  // then every lane whose block starts a word has the word's other blocks
+  const bool sf_words = (reinterpret_cast<uintptr_t>(sf) & 3) == 0 && (kMX ? nblk % 8 : nblk % 4) == 0;
   // Destinations in batches of 8 (scalar loads shared by the wavefront): the
   // batch's expert ids and rows, then their SFScaleVals, are fetched before
   // any encoding, so the load latencies overlap.
@@ -78,18 +81,39 @@ __global__ __launch_bounds__(1024) void quantize_experts_kernel(
 #pragma unroll
     for (int jj = 0; jj < kBatch; ++jj) {
       const int32_t e = eb[jj], p = pb[jj];
+      // wave-uniform skip (every lane sees the same destination), so the
+      // whole wavefront takes part in the scale-byte exchange below
       if (j0 + jj >= topk || (uint32_t)p >= (uint32_t)num_dst_rows ||
-          (uint32_t)e >= (uint32_t)num_experts || !on)
+          (uint32_t)e >= (uint32_t)num_experts)
         continue;
       const BlockScale bs = kMX ? block_scale_ue8m0(a6, gb[jj]) : block_scale(a6, gb[jj]);
-      uint2 w;
-      w.x = encode8(xv, bs.inv);
-      w.y = encode8(xv + 8, bs.inv);
-      *reinterpret_cast<uint2*>(codes + (int64_t)p * row_bytes + (int64_t)b * 8) = w;
-      if constexpr (kMX) {
-        if ((b & 1) == 0) sf[(int64_t)p * (nblk / 2) + b / 2] = (uint8_t)bs.sf;
-      } else {
-        sf[(int64_t)p * nblk + b] = (uint8_t)bs.sf;
+      if (on) {
+        uint2 w;
+        w.x = encode8(xv, bs.inv);
+        w.y = encode8(xv + 8, bs.inv);
+        *reinterpret_cast<uint2*>(codes + (int64_t)p * row_bytes + (int64_t)b * 8) = w;
+      }
+      // Scale bytes, four per 32-bit store: lane b collects the bytes of the
+      // next three blocks with two DPP moves (E4M3: lanes b+1..b+3; UE8M0,
+      // where both lanes of a pair hold their block's byte: b+2, b+4, b+6).
+      if (sf_words) {
+        uint32_t v = bs.sf;
+        if constexpr (kMX) {
+          v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false) << 8;
+          v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x104, 0xF, 0xF, false) << 16;
+          if (on && (b & 7) == 0)
+            *reinterpret_cast<uint32_t*>(sf + (int64_t)p * (nblk / 2) + b / 2) = v;
+        } else {
+          v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false) << 8;
+          v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false) << 16;
+          if (on && (b & 3) == 0) *reinterpret_cast<uint32_t*>(sf + (int64_t)p * nblk + b) = v;
+        }
+      } else if (on) {
+        if constexpr (kMX) {
+          if ((b & 1) == 0) sf[(int64_t)p * (nblk / 2) + b / 2] = (uint8_t)bs.sf;
+        } else {
+          sf[(int64_t)p * nblk + b] = (uint8_t)bs.sf;
+        }
       }
     }
   }

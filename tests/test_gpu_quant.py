@@ -223,3 +223,40 @@ def test_weight_packing_layout(projection):
     rc, rs = _pack_reference(codes, sf, 128 if projection == 0 else 64)
     assert np.array_equal(oc.cpu().numpy().reshape(-1), rc)
     assert np.array_equal(osf.cpu().numpy().reshape(-1), rs)
+
+
+@pytest.mark.parametrize("mx", [False, True])
+@pytest.mark.parametrize("blocks,offset", [(21, 0), (20, 0), (20, 1), (43, 3)])
+def test_scale_words_and_byte_fallback(mx, blocks, offset):
+    """Scale bytes leave as 32-bit words when the row's scale count is a
+    multiple of 4 (8 blocks of 16 in the UE8M0 mode) and the array is
+    4-byte aligned, else one byte at a time: odd widths and a misaligned
+    scale array, both modes, bit-exact against the oracle."""
+    torch = _torch()
+    from nvfp4_w4a4_expert_amd import _lib as L
+    from nvfp4_w4a4_expert_amd import moe as M
+    from oracle import mx as OX
+    blk = 32 if mx else 16
+    K = blk * blocks
+    rng = np.random.default_rng(blocks * 10 + offset + (100 if mx else 0))
+    T, E, k = 40, 6, 3
+    x = S.f32_to_bf16_bits((rng.standard_normal((T, K)) * 10.0 ** rng.uniform(-3, 3, (T, 1)))
+                           .astype(np.float32))
+    ids, _ = OM.route(rng.standard_normal((T, E)).astype(np.float32), k)
+    offsets, src, inv = OM.permute(ids, E)
+    gs = (10.0 ** rng.uniform(-2, 2, E)).astype(np.float32)
+    P = T * k
+    codes = torch.full((P, K // 2), 0xAB, dtype=torch.uint8, device="cuda")
+    sf_buf = torch.full((P * (K // blk) + 8,), 0xCD, dtype=torch.uint8, device="cuda")
+    sf = sf_buf[offset:offset + P * (K // blk)]
+    fn = L.quantize_experts_mx if mx else L.quantize_experts
+    dev = lambda a, t: torch.from_numpy(np.ascontiguousarray(a, dtype=t)).cuda()
+    fn(M.bf16_tensor(x), K, T, K, k, dev(ids, np.int32), dev(inv, np.int32), E, dev(gs, np.float32),
+       codes, sf, P)
+    torch.cuda.synchronize()
+    Q = OX if mx else OQ
+    oc, osf = Q.quantize_experts(x[src // k], OM.row_experts(offsets), gs)
+    assert np.array_equal(sf.cpu().numpy().reshape(P, K // blk), osf)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    rest = sf_buf.cpu().numpy()
+    assert np.all(rest[:offset] == 0xCD) and np.all(rest[offset + P * (K // blk):] == 0xCD)
