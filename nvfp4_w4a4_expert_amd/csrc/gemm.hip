@@ -210,7 +210,8 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
 
   // ---- once per workgroup: per-expert m-tile prefix in LDS -----------------
   {
-    constexpr int kPer = (kMaxExperts + kThreads - 1) / kThreads;
+    // entries 0 .. E of the prefix (E + 1 <= kMaxExperts + 1 of them)
+    constexpr int kPer = (kMaxExperts + 1 + kThreads - 1) / kThreads;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int32_t cnt[kPer], total = 0;
 #pragma unroll
@@ -271,6 +272,7 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
   }
   const int32_t row0 = s_off[e] + (mt - s_mt[e]) * kBM;
   const int32_t rows = min(kBM, s_off[e + 1] - row0);
+  if (rows <= 0) continue;                             // (uniform; never for consistent offsets)
 
   // ---- B streaming assignment: wave's 64 weight rows, 2 blocks of 32 ------
   // GEMM1: block 0 = gate rows, block 1 = the matching up rows.  Weights are

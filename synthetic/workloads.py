@@ -65,6 +65,10 @@ WORKLOADS = {
                         outlier_frac=0.005, outlier_gain=30.0, calib_tokens=512, layer_wid=3),
     "stack": Workload("stack", 5, T=8192, H=2816, E=128, I=704, k=8, layers=30, router="zipf",
                       calib_tokens=512),
+    # the boundary's largest expert count and top-k on a small hidden size: the
+    # small-batch GEMM path at 96 tokens, the large one at 1024 (P = 32 E)
+    "maxsize": Workload("maxsize", 6, T=1024, H=256, E=1024, I=128, k=32, router="normal",
+                        calib_tokens=1024),
 }
 
 

@@ -110,3 +110,16 @@ def test_stack_layer(layer_idx):
     m = check_layer_parity(layer, x, logits, w.k, residual_bits=x, label=f"stack L{layer_idx}")
     assert np.count_nonzero(np.diff(m["ref"]["offsets"]) == 0) >= 1
     _report(f"stack L{layer_idx}", m)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T", [96, 1024])
+def test_max_experts_and_topk(T):
+    """E = 1024 experts (the boundary's limit) and k = 32: the small-batch
+    GEMM path at 96 tokens and the large one at 1024 tokens (P = 32 E)."""
+    w = S.WORKLOADS["maxsize"]
+    layer = oracle_layer("maxsize")
+    x = S.activations(w, tokens=T)
+    logits = S.router_logits(w, tokens=T)
+    m = check_layer_parity(layer, x, logits, w.k, label=f"maxsize T={T}")
+    _report(f"maxsize T={T}", m)

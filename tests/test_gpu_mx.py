@@ -149,3 +149,12 @@ def test_mx_prefill_layer():
     m = check_layer_parity(oracle_layer_mx("prefill"), S.activations(w), S.router_logits(w),
                            w.k, label="mx prefill", mx=True)
     _report("mx prefill", m)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T", [96, 1024])
+def test_mx_max_experts_and_topk(T):
+    w = S.WORKLOADS["maxsize"]
+    m = check_layer_parity(oracle_layer_mx("maxsize"), S.activations(w, tokens=T),
+                           S.router_logits(w, tokens=T), w.k, label=f"mx maxsize T={T}", mx=True)
+    _report(f"mx maxsize T={T}", m)

@@ -120,3 +120,12 @@ def test_w4a16_prefill_layer():
     m = check_layer_parity_w4a16(oracle_layer("prefill"), S.activations(w), S.router_logits(w),
                                  w.k, label="w4a16 prefill")
     _report("w4a16 prefill", m)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T", [96, 1024])
+def test_w4a16_max_experts_and_topk(T):
+    w = S.WORKLOADS["maxsize"]
+    m = check_layer_parity_w4a16(oracle_layer("maxsize"), S.activations(w, tokens=T),
+                                 S.router_logits(w, tokens=T), w.k, label=f"w4a16 maxsize T={T}")
+    _report(f"w4a16 maxsize T={T}", m)
