@@ -69,6 +69,10 @@ WORKLOADS = {
     # small-batch GEMM path at 96 tokens, the large one at 1024 (P = 32 E)
     "maxsize": Workload("maxsize", 6, T=1024, H=256, E=1024, I=128, k=32, router="normal",
                         calib_tokens=1024),
+    # K-step counts that are not multiples of the register-ring depth in either
+    # GEMM (w13: 5 steps of 128, w2: 5 steps of 64) and a skewed router
+    "shapes": Workload("shapes", 7, T=200, H=640, E=8, I=320, k=3, router="normal_bias",
+                       calib_tokens=512),
 }
 
 

@@ -175,6 +175,25 @@ def test_w4a16_workspace_holds_bf16_h_instead_of_codes():
     assert b - P * (704 * 2 + 2816 * 4 + 16) < 8 * 256 + 129 * 4
 
 
+def test_ue8m0_mode_host_checks():
+    L = _lib()
+    f = L._lib
+    fake = 4096
+    # hidden must be a multiple of 256 in the UE8M0 mode (w13 K step), 128 otherwise
+    assert f.nvfp4_moe_pack_weights_mx(0, fake, fake, 8, 640, 320, 2 * fake, 2 * fake, None) \
+        == L.ERR_UNSUPPORTED
+    w = L.MoEWeights(*([fake] * 10), 8, 640, 320)
+    assert f.nvfp4_moe_forward_mx(ctypes.byref(w), fake, fake, 4, 2, None, fake, fake, 1 << 30,
+                                  None, None) == L.ERR_UNSUPPORTED
+    # K not a multiple of 32 in the UE8M0 quantiser
+    assert f.nvfp4_quantize_experts_mx(16, 48, 1, 48, 1, None, None, 1, None, 16, 16, 1, None) \
+        == L.ERR_INVALID_ARG
+    # the activation scales are required, as in the E4M3 mode
+    w = L.MoEWeights(*([fake] * 6), 0, 0, 0, 0, 4, 256, 128)
+    assert f.nvfp4_moe_forward_mx(ctypes.byref(w), fake, fake, 4, 2, None, fake, fake, 1 << 30,
+                                  None, None) == L.ERR_INVALID_ARG
+
+
 def test_bad_scales_are_rejected_before_upload():
     from nvfp4_w4a4_expert_amd import moe as M
     import synthetic as S

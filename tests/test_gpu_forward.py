@@ -123,3 +123,28 @@ def test_max_experts_and_topk(T):
     logits = S.router_logits(w, tokens=T)
     m = check_layer_parity(layer, x, logits, w.k, label=f"maxsize T={T}")
     _report(f"maxsize T={T}", m)
+
+
+def test_ring_tails_and_skewed_router():
+    """hidden 640 / intermediate 320: both GEMMs end on a partial group of
+    register-ring steps; a biased router concentrates rows on a few experts."""
+    w = S.WORKLOADS["shapes"]
+    layer = oracle_layer("shapes")
+    m = check_layer_parity(layer, S.activations(w), S.router_logits(w), w.k, label="shapes")
+    _report("shapes", m)
+
+
+def test_all_rows_on_two_experts():
+    """Every token routed to experts 0 and 1: many m-tiles of one expert, six
+    experts without rows."""
+    w = S.WORKLOADS["tiny"]
+    layer = oracle_layer("tiny")
+    rng = np.random.default_rng(31)
+    T = 300
+    x = S.f32_to_bf16_bits(rng.standard_normal((T, w.H)).astype(np.float32))
+    logits = rng.standard_normal((T, w.E)).astype(np.float32) - 40.0
+    logits[:, 0] += 80.0
+    logits[:, 1] += 60.0
+    m = check_layer_parity(layer, x, logits, 2, label="two experts")
+    counts = np.diff(m["ref"]["offsets"])
+    assert counts[0] == T and counts[1] == T and counts[2:].sum() == 0

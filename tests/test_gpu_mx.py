@@ -158,3 +158,4 @@ def test_mx_max_experts_and_topk(T):
     m = check_layer_parity(oracle_layer_mx("maxsize"), S.activations(w, tokens=T),
                            S.router_logits(w, tokens=T), w.k, label=f"mx maxsize T={T}", mx=True)
     _report(f"mx maxsize T={T}", m)
+

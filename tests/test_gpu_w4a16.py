@@ -129,3 +129,10 @@ def test_w4a16_max_experts_and_topk(T):
     m = check_layer_parity_w4a16(oracle_layer("maxsize"), S.activations(w, tokens=T),
                                  S.router_logits(w, tokens=T), w.k, label=f"w4a16 maxsize T={T}")
     _report(f"w4a16 maxsize T={T}", m)
+
+
+def test_w4a16_ring_tails():
+    w = S.WORKLOADS["shapes"]
+    m = check_layer_parity_w4a16(oracle_layer("shapes"), S.activations(w), S.router_logits(w),
+                                 w.k, label="w4a16 shapes")
+    _report("w4a16 shapes", m)
