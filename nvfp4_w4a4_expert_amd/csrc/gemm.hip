@@ -104,10 +104,22 @@ constexpr int kG1Waves = 8, kG1MB = 2, kG1BK = 128, kG1Ring = 3, kG1Occ = 1;
 // too little matrix work per barrier and per prefetch slot)
 constexpr int kG1BKmx = 256;
 constexpr int kG2MB = 4, kG2Ring = 2, kG2Occ = 2;
+// Batches with fewer than 32 rows per expert on average (decode): one 32-row
+// sub-tile, 4 wavefronts, 2 workgroups per CU; ring depth for w13 / w2.
+constexpr int kS1Ring = 3, kS2Ring = 3;
 constexpr int kMaxExperts = 1024;
 
 template <int V>
 using Int = std::integral_constant<int, V>;
+
+// f(Int<0>{}), f(Int<1>{}), ..., f(Int<N-1>{}), in that order.
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(Int<N - 1>{});
+  }
+}
 
 // 8 E2M1 codes (one 32-bit word) -> 8 exact fp16 values scaled by `s`.
 __device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t s) {
@@ -551,14 +563,12 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
   // of kRing steps loop with no early exit (so accumulators stay in place);
   // the remaining steps follow.
   // prologue in the steady state's issue order (A then B of each step)
-  load_a(0, Int<0>{});
-  load_b(0, Int<0>{});
-  load_a(min(1, nk - 1), Int<1>{});
-  load_b(min(1, nk - 1), Int<1>{});
-  if constexpr (kRing > 2) {
-    load_a(min(2, nk - 1), Int<2 % kRing>{});
-    load_b(min(2, nk - 1), Int<2 % kRing>{});
-  }
+  static_assert(kRing >= 2, "at least two ring slots");
+  static_for<kRing>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    load_a(min(i, nk - 1), Int<i>{});
+    load_b(min(i, nk - 1), Int<i>{});
+  });
   store_a(0, Int<0>{});
   lds_barrier();
   auto step = [&](int kt, auto rc) {
@@ -579,13 +589,12 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
     lds_barrier();
   };
   const int nkr = nk - nk % kRing;
-  for (int kt = 0; kt < nkr; kt += kRing) {
-    step(kt, Int<0>{});
-    step(kt + 1, Int<1 % kRing>{});
-    if constexpr (kRing > 2) step(kt + 2, Int<2 % kRing>{});
-  }
-  if (nkr < nk) step(nkr, Int<0>{});
-  if constexpr (kRing > 2) if (nkr + 1 < nk) step(nkr + 1, Int<1>{});
+  for (int kt = 0; kt < nkr; kt += kRing)
+    static_for<kRing>([&](auto ic) { step(kt + decltype(ic)::value, ic); });
+  static_for<kRing - 1>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if (nkr + i < nk) step(nkr + i, ic);
+  });
 
   const float alpha = kW16 ? prm.w_scale2[e] : prm.in_scale[e] * prm.w_scale2[e];
   // MFMA 32x32 output layout: lane holds column (lane & 31) and rows
@@ -816,8 +825,9 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream) {
   }
   constexpr int kWaves = 4;
   prm.n_tiles = (a.I + 32 * kWaves - 1) / (32 * kWaves);
-#define NVFP4_G1(m) return launch<kWaves, 1, kG1BK, true, 3, 2, m>(prm, a.P, stream)
-  if (mode == kModeMX) return launch<kWaves, 1, kG1BKmx, true, 3, 2, kModeMX>(prm, a.P, stream);
+#define NVFP4_G1(m) return launch<kWaves, 1, kG1BK, true, kS1Ring, 2, m>(prm, a.P, stream)
+  if (mode == kModeMX)
+    return launch<kWaves, 1, kG1BKmx, true, kS1Ring, 2, kModeMX>(prm, a.P, stream);
   if (mode == kModeW16) NVFP4_G1(kModeW16);
   NVFP4_G1(kModeNV);
 #undef NVFP4_G1
@@ -841,7 +851,7 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream) {
     NVFP4_G2(kModeNV);
 #undef NVFP4_G2
   }
-#define NVFP4_G2(m) return launch<kWaves, 1, 64, false, 3, 2, m>(prm, a.P, stream)
+#define NVFP4_G2(m) return launch<kWaves, 1, 64, false, kS2Ring, 2, m>(prm, a.P, stream)
   if (mode == kModeMX) NVFP4_G2(kModeMX);
   if (mode == kModeW16) NVFP4_G2(kModeW16);
   NVFP4_G2(kModeNV);
