@@ -768,8 +768,8 @@ int32_t m_tiles_bound(int32_t P, int32_t E, int32_t bm) {
   return (P + bm - 1) / bm + (P < E ? P : E);
 }
 
-// Resident workgroups per CU for a kernel, and the CU count, looked up once
-// per process for the current device.
+// Resident workgroups per CU for a kernel, and the CU count, for the current
+// device (every device this library runs on is the same gfx950 part).
 struct Residency {
   int cus = 0, per_cu = 0;
 };
@@ -777,7 +777,21 @@ struct Residency {
 template <int kWaves, int kMB, int kBK, bool kGated, int kRing, int kOcc, int kMode>
 hipError_t launch(GemmParams prm, int32_t P, hipStream_t stream) {
   constexpr int kBM = 32 * kMB;
-  static Residency res;
+  // looked up once per process (a function-local static is initialised once,
+  // thread-safely); a failed lookup is retried on the next call
+  static const Residency cached = [] {
+    Residency r;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&r.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &r.per_cu, (const void*)grouped_gemm_kernel<kWaves, kMB, kBK, kGated, kRing, kOcc, kMode>,
+            64 * kWaves, 0) != hipSuccess)
+      return Residency{};
+    if (r.per_cu < 1) r.per_cu = 1;
+    return r;
+  }();
+  Residency res = cached;
   if (res.cus == 0) {
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);

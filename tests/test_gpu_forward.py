@@ -148,3 +148,45 @@ def test_all_rows_on_two_experts():
     m = check_layer_parity(layer, x, logits, 2, label="two experts")
     counts = np.diff(m["ref"]["offsets"])
     assert counts[0] == T and counts[1] == T and counts[2:].sum() == 0
+
+
+def test_concurrent_forwards_from_two_host_threads():
+    """Two host threads, each with its own stream (default priority),
+    workspace and layer object, run forwards at the same time: every output
+    equals the serial one bit for bit."""
+    import threading
+    import torch
+    from nvfp4_w4a4_expert_amd import moe as M
+    w = S.WORKLOADS["tiny"]
+    layer = oracle_layer("tiny")
+    xs = [M.bf16_tensor(S.activations(w, layer=i)) for i in range(4)]
+    lgs = [torch.from_numpy(S.router_logits(w, layer=i)).cuda() for i in range(4)]
+    ref_layer = device_layer(layer)
+    ref = [ref_layer.forward(xs[i], lgs[i], w.k).clone() for i in range(4)]
+    torch.cuda.synchronize()
+    results = {}
+    errors = []
+
+    def worker(tid):
+        try:
+            dl = device_layer(layer)
+            stream = torch.cuda.Stream()
+            outs = []
+            with torch.cuda.stream(stream):
+                for rep in range(10):
+                    i = (tid + rep) % 4
+                    outs.append((i, dl.forward(xs[i], lgs[i], w.k, stream=stream.cuda_stream)))
+            stream.synchronize()
+            results[tid] = outs
+        except Exception as e:                      # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for tid in range(2):
+        for i, out in results[tid]:
+            assert torch.equal(out.view(torch.int16), ref[i].view(torch.int16))
