@@ -48,7 +48,7 @@ def parse_args():
                     help="skip the weight-only (W4A16) sub-measurement")
     ap.add_argument("--no-mx", action="store_true",
                     help="skip the UE8M0 (MX-style) sub-measurement")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
                          "known-size reference for the FETCH_SIZE / WRITE_SIZE counters)")
