@@ -298,11 +298,13 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 hipError_t launch_permute(const int32_t* ids, int32_t P, int32_t E, int32_t* offsets,
                           int32_t* src_pair, int32_t* inv, hipStream_t stream) {
   if (E < 1 || E > kPermMaxE || P < 0) return hipErrorInvalidValue;
-  // Blocks of at least 2048 pairs; at most 256 of them, so the all-pairs
-  // histogram each workgroup builds stays a small multiple of P.
+  // Blocks of at least 512 pairs (one ranking step per workgroup: measured
+  // 16.4 -> 13.3 us at 32768 pairs against 2048-pair blocks); at most 256 of
+  // them, so the all-pairs histogram each workgroup builds stays a small
+  // multiple of P.
   int64_t span = ((int64_t)P + 255) / 256;
   span = (span + kPermThreads - 1) / kPermThreads * kPermThreads;
-  if (span < 2048) span = 2048;
+  if (span < kPermThreads) span = kPermThreads;
   const int32_t blocks = P == 0 ? 1 : (int32_t)(((int64_t)P + span - 1) / span);
   int32_t id_bits = 0;
   while ((1 << id_bits) < E) ++id_bits;
