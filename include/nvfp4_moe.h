@@ -346,7 +346,9 @@ NVFP4_API nvfp4_status_t nvfp4_moe_workspace_size(int32_t num_tokens, int32_t k,
  *   out_bf16       device bf16 [T, H]; may alias residual_bf16 or x_bf16.
  *   workspace      device, 256-byte aligned, >= nvfp4_moe_workspace_size().
  *   debug          NULL or buffers for intermediates.
- * Requirements: H % 128 == 0, I % 64 == 0, 1 <= k <= min(E, 32), E <= 1024.
+ * Requirements: H % 128 == 0, I % 64 == 0, 1 <= k <= min(E, 32), E <= 1024,
+ * T*k <= 2^30, and (ceil(T*k/32) + min(T*k, E)) * max(ceil(I/128), ceil(H/256))
+ * <= 2^31 - 1 (the GEMM tile count); else NVFP4_ERR_UNSUPPORTED.
  * T == 0 is a no-op.  Experts that receive no rows cost nothing.
  */
 NVFP4_API nvfp4_status_t nvfp4_moe_forward(const nvfp4_moe_weights_t* w, const void* x_bf16,

@@ -1,5 +1,7 @@
 // C ABI of libnvfp4moe.so: argument checking, the load-time scale check,
 // workspace layout and the launch sequence of one MoE layer.
+#include <algorithm>
+#include <cstdint>
 #include <math.h>
 #include <string.h>
 
@@ -312,6 +314,14 @@ nvfp4_status_t moe_forward(const nvfp4_moe_weights_t* w, const void* x_bf16,
   if (num_tokens < 0 || k < 1 || k > E) return NVFP4_ERR_INVALID_ARG;
   if (k > 32) return NVFP4_ERR_UNSUPPORTED;
   if ((int64_t)num_tokens * k > (1 << 30)) return NVFP4_ERR_UNSUPPORTED;
+  // the GEMM kernels number their (m-tile, n-tile) pairs in 32 bits: bound
+  // them for the smallest tiles (32 rows; 128 h columns, 256 output columns)
+  {
+    const int64_t P = (int64_t)num_tokens * k;
+    const int64_t m_tiles = (P + 31) / 32 + (P < E ? P : E);
+    const int64_t n_tiles = std::max(((int64_t)I + 127) / 128, ((int64_t)H + 255) / 256);
+    if (m_tiles * n_tiles > INT32_MAX) return NVFP4_ERR_UNSUPPORTED;
+  }
   if (num_tokens == 0) return NVFP4_OK;
   if (!x_bf16 || !router_logits || !out_bf16) return NVFP4_ERR_INVALID_ARG;
   if (!aligned(x_bf16, 16) || !aligned(out_bf16, 16) ||

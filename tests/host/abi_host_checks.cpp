@@ -237,6 +237,15 @@ static void forward_checks() {
   bad.inter = 320;
   CHECK(nvfp4_moe_forward_mx(&bad, x, logits, T, k, nullptr, out, ws, ws_bytes, nullptr,
                              nullptr) == NVFP4_ERR_UNSUPPORTED);
+  // GEMM tile count past 32 bits (2^29 pairs, hidden 2^20): refused; the
+  // largest pair count at this layer's widths passes that check and stops at
+  // the workspace size
+  bad = w;
+  bad.hidden = 1 << 20;
+  CHECK(nvfp4_moe_forward(&bad, x, logits, 1 << 26, k, nullptr, out, ws, ws_bytes, nullptr,
+                          nullptr) == NVFP4_ERR_UNSUPPORTED);
+  CHECK(nvfp4_moe_forward(&w, x, logits, (1 << 30) / k, k, nullptr, out, ws, ws_bytes, nullptr,
+                          nullptr) == NVFP4_ERR_WORKSPACE);
   bad = w;
   bad.num_experts = 1025;
   CHECK(nvfp4_moe_forward(&bad, x, logits, T, k, nullptr, out, ws, ws_bytes, nullptr, nullptr) ==
