@@ -22,14 +22,37 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int32_t t = (int32_t)(g / h8);
   const int32_t c = (int32_t)(g - (int64_t)t * h8) * 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int32_t j = 0; j < k; ++j) {
-    const int64_t q = (int64_t)t * k + j;
-    const float wj = w[q];
-    const f32x4* src = reinterpret_cast<const f32x4*>(c2 + (int64_t)inv[q] * H + c);
-    const f32x4 a = __builtin_nontemporal_load(src);
-    const f32x4 b = __builtin_nontemporal_load(src + 1);
-    acc[0] += wj * a.x; acc[1] += wj * a.y; acc[2] += wj * a.z; acc[3] += wj * a.w;
-    acc[4] += wj * b.x; acc[5] += wj * b.y; acc[6] += wj * b.z; acc[7] += wj * b.w;
+  // Slots in groups of kU: the group's row indices first, then all its row
+  // loads, then the sums in slot order (slots past k re-read row k-1 and are
+  // not added), so each thread keeps 2 kU loads in flight instead of a chain
+  // of index load -> row load per slot.
+  constexpr int kU = 8;
+  const int64_t q0 = (int64_t)t * k;
+  for (int32_t j0 = 0; j0 < k; j0 += kU) {
+    int32_t row[kU];
+    float wj[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int32_t j = min(j0 + u, k - 1);
+      row[u] = inv[q0 + j];
+      wj[u] = w[q0 + j];
+    }
+    f32x4 a[kU], b[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(c2 + (int64_t)row[u] * H + c);
+      a[u] = __builtin_nontemporal_load(src);
+      b[u] = __builtin_nontemporal_load(src + 1);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (j0 + u < k) {
+        acc[0] += wj[u] * a[u].x; acc[1] += wj[u] * a[u].y;
+        acc[2] += wj[u] * a[u].z; acc[3] += wj[u] * a[u].w;
+        acc[4] += wj[u] * b[u].x; acc[5] += wj[u] * b[u].y;
+        acc[6] += wj[u] * b[u].z; acc[7] += wj[u] * b[u].w;
+      }
+    }
   }
   if (residual) {
     const uint4 r = *reinterpret_cast<const uint4*>(residual + (int64_t)t * H + c);
