@@ -589,8 +589,17 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
     // would defeat the ring.
     load_a(min(kt + kRing, nk - 1), Int<r>{});
     if (active) {
-      store_a((kt + 1) & 1, Int<rn>{});
-      compute(kt & 1, Int<r>{});
+      // the large-batch w2 issues its MFMAs before staging the next token
+      // step (the staging's load wait then overlaps them: 182 -> 178 us at the
+      // prefill layer); w13 and the small-batch kernels measured better the
+      // other way round
+      if constexpr (kGated || kMB == 1) {
+        store_a((kt + 1) & 1, Int<rn>{});
+        compute(kt & 1, Int<r>{});
+      } else {
+        compute(kt & 1, Int<r>{});
+        store_a((kt + 1) & 1, Int<rn>{});
+      }
     } else {
       store_a((kt + 1) & 1, Int<rn>{});
     }
