@@ -16,6 +16,8 @@ from oracle import moe as M
 from oracle import quant as Q
 import synthetic as S
 
+from pin_helpers import identity_w13, token_major_w4a4, tiny_layer_with_distinct_scales
+
 
 # --- validator ---------------------------------------------------------------
 
@@ -329,3 +331,58 @@ def test_w4a16_layer_is_token_major_definition_and_ignores_input_scales():
     e16 = np.linalg.norm(r["out_f64"] - S.bf16_bits_to_f32(res) - ref_r)
     e4 = np.linalg.norm(r4["out_f64"] - S.bf16_bits_to_f32(res) - ref_r)
     assert e16 < e4
+
+
+# --- W4A4 layer: token-major definition with the GEMM scalings written out ----
+
+def test_w4a4_layer_is_token_major_definition_with_alpha_written_out():
+    w, layer = tiny_layer_with_distinct_scales(M.prepare_layer)
+    x = S.activations(w)
+    logits = S.router_logits(w)
+    rng = np.random.default_rng(33)
+    res = S.f32_to_bf16_bits(rng.standard_normal((w.T, w.H)).astype(np.float32))
+    r = M.layer_forward(layer, x, logits, w.k, residual_bits=res)
+    ref = token_major_w4a4(layer, x, logits, w.k, res, Q.quantize_bf16_rows, Q.dequant)
+    assert np.allclose(r["out_f64"], ref, rtol=1e-12, atol=1e-12)
+    # the pin separates the plausible mistakes by orders of magnitude
+    base = S.bf16_bits_to_f32(res).astype(np.float64)
+    scale = np.linalg.norm(ref - base)
+    for kw in (dict(swap_alpha=True), dict(a2_with_a1_scale=True)):
+        wrong = token_major_w4a4(layer, x, logits, w.k, res, Q.quantize_bf16_rows, Q.dequant,
+                                  **kw)
+        assert np.linalg.norm(wrong - ref) > 0.05 * scale, kw
+
+
+# --- calibration: closed form of the w2 activation scale ------------------------
+
+def test_calibration_w2_scale_closed_form():
+    """w2_input_scale[e] = fl32(fl32(max |h|) / 2688) with h = silu(gate) * up
+    over the calibration rows routed to e.  With gate = x and up = 2x
+    (identity-like w13), max |h| = max 2 x^2 / (1 + e^-x) over the rows, in
+    closed form; an expert with no rows stays unwritten."""
+    E, I, H, k = 3, 16, 32, 1
+    w13c, w13s, w13s2 = identity_w13(E, I, H, 1.0, 2.0)
+    w2c = np.zeros((E, H, I // 2), dtype=np.uint8)
+    w2s = np.full((E, H, I // 16), 0x38, dtype=np.uint8)
+    w2s2 = np.ones(E, dtype=np.float32)
+    rng = np.random.default_rng(41)
+    T = 12
+    xf = (rng.standard_normal((T, H)) * 2).astype(np.float32)
+    x = S.f32_to_bf16_bits(xf)
+    xv = S.bf16_bits_to_f32(x).astype(np.float64)
+    logits = np.full((T, E), -5.0, dtype=np.float32)
+    logits[np.arange(T), np.arange(T) % 2] = 5.0       # tokens alternate experts 0 and 1
+    s13, s2, written = M.calibrate(x, logits, k, w13c, w13s, w13s2, w2c, w2s, w2s2)
+    assert written.tolist() == [1, 1, 0]
+    assert np.isnan(s13[2]) and np.isnan(s2[2])
+    for e in (0, 1):
+        rows = xv[np.arange(T) % 2 == e][:, :I]       # only the first I channels feed h
+        h = [2.0 * v * v / (1.0 + math.exp(-v)) for v in rows.reshape(-1)]
+        amax_h = max(abs(v) for v in h)
+        assert s2[e] == np.float32(np.float32(amax_h) / np.float32(2688.0))
+        amax_x = float(np.abs(xv[np.arange(T) % 2 == e]).max())
+        assert s13[e] == np.float32(np.float32(amax_x) / np.float32(2688.0))
+    # the gate/up order matters: silu(2x) * x differs from silu(x) * 2x
+    w13c_sw, _, _ = identity_w13(E, I, H, 2.0, 1.0)
+    _, s2_sw, _ = M.calibrate(x, logits, k, w13c_sw, w13s, w13s2, w2c, w2s, w2s2)
+    assert not np.array_equal(s2_sw[:2], s2[:2])

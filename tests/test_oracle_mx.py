@@ -17,6 +17,8 @@ from oracle import mx as X
 from oracle import quant as Q
 import synthetic as S
 
+from pin_helpers import identity_w13, token_major_w4a4, tiny_layer_with_distinct_scales
+
 
 def _f32(v):
     return np.float32(v)
@@ -143,22 +145,23 @@ def test_mx_layer_token_major_and_close_to_unquantised():
     x = S.activations(w)
     logits = S.router_logits(w)
     r = X.layer_forward(layer, x, logits, w.k)
-    # token-major definition over the same quantised operands
     ids, wts = M.route(logits, w.k)
-    ok, g1, _ = M.validate_scales(layer.w13_input_scale, layer.written13)
-    ok2, g2, _ = M.validate_scales(layer.w2_input_scale, layer.written2)
-    assert ok and ok2
-    ref = np.zeros((w.T, w.H))
-    for t in range(w.T):
-        for j in range(w.k):
-            e = ids[t, j]
-            ac, asf = X.quantize_bf16_rows(x[t:t + 1], np.array([g1[e]], dtype=np.float32))
-            c1 = layer.alpha1[e] * (X.dequant(ac, asf) @ X.dequant(layer.w13c[e], layer.w13s[e]).T)
-            hb = F.f64_to_bf16(M.silu_mul(c1, w.I))
-            a2c, a2s = X.quantize_bf16_rows(hb, np.array([g2[e]], dtype=np.float32))
-            c2 = layer.alpha2[e] * (X.dequant(a2c, a2s) @ X.dequant(layer.w2c[e], layer.w2s[e]).T)
-            ref[t] += wts[t, j] * c2[0]
-    assert np.allclose(r["out_f64"], ref, rtol=1e-12, atol=1e-12)
+    # token-major definition over the same quantised operands, with the
+    # scalings written out (alpha = input_scale x weight_scale_2 of the same
+    # projection, SFScaleVal = fl32(1 / input_scale)): pinned on a layer whose
+    # w2 weights are 2^3 larger, so a swapped alpha or a wrong SFScaleVal
+    # cannot pass
+    w_d, layer_d = tiny_layer_with_distinct_scales(X.prepare_layer)
+    rng = np.random.default_rng(34)
+    res = S.f32_to_bf16_bits(rng.standard_normal((w.T, w.H)).astype(np.float32))
+    r_d = X.layer_forward(layer_d, x, logits, w.k, residual_bits=res)
+    ref_d = token_major_w4a4(layer_d, x, logits, w.k, res, X.quantize_bf16_rows, X.dequant)
+    assert np.allclose(r_d["out_f64"], ref_d, rtol=1e-12, atol=1e-12)
+    base = S.bf16_bits_to_f32(res).astype(np.float64)
+    for kw in (dict(swap_alpha=True), dict(a2_with_a1_scale=True)):
+        wrong = token_major_w4a4(layer_d, x, logits, w.k, res, X.quantize_bf16_rows, X.dequant,
+                                 **kw)
+        assert np.linalg.norm(wrong - ref_d) > 0.05 * np.linalg.norm(ref_d - base), kw
     # the MX layer tracks the unquantised fp64 layer (coarser than E4M3 scales)
     xf = S.bf16_bits_to_f32(x).astype(np.float64)
     exact = np.zeros((w.T, w.H))
@@ -177,3 +180,29 @@ def test_mx_layer_token_major_and_close_to_unquantised():
                     np.zeros(w.E, dtype=np.uint8), layer.written2)
     with pytest.raises(ValueError):
         X.layer_forward(bad, x, logits, w.k)
+
+
+def test_mx_calibration_w2_scale_closed_form():
+    """The UE8M0 layer's calibration: w2_input_scale[e] = fl32(fl32(max |h|) /
+    2688) with h = silu(gate) * up of the rows routed to e; with gate = x and
+    up = 2x (identity-like w13 at unit UE8M0 scales) max |h| has a closed
+    form.  An expert without rows stays unwritten."""
+    E, I, H, k = 3, 32, 64, 1
+    w13c, w13s, w13s2 = identity_w13(E, I, H, 1.0, 2.0, block=32, unit_code=127)
+    assert np.array_equal(X.dequant(w13c[0], w13s[0])[:I, :I], np.eye(I))
+    w2c = np.zeros((E, H, I // 2), dtype=np.uint8)
+    w2s = np.full((E, H, I // 32), 127, dtype=np.uint8)
+    rng = np.random.default_rng(43)
+    T = 10
+    x = S.f32_to_bf16_bits((rng.standard_normal((T, H)) * 2).astype(np.float32))
+    xv = S.bf16_bits_to_f32(x).astype(np.float64)
+    logits = np.full((T, E), -5.0, dtype=np.float32)
+    logits[np.arange(T), 2 * (np.arange(T) % 2)] = 5.0      # experts 0 and 2; 1 gets none
+    s13, s2, written = X.calibrate(x, logits, k, w13c, w13s, w13s2, w2c, w2s,
+                                   np.ones(E, dtype=np.float32))
+    assert written.tolist() == [1, 0, 1] and np.isnan(s2[1]) and np.isnan(s13[1])
+    for e in (0, 2):
+        rows = xv[2 * (np.arange(T) % 2) == e]
+        amax_h = max(abs(2.0 * v * v / (1.0 + math.exp(-v))) for v in rows[:, :I].reshape(-1))
+        assert s2[e] == np.float32(np.float32(amax_h) / np.float32(2688.0))
+        assert s13[e] == np.float32(np.float32(np.abs(rows).max()) / np.float32(2688.0))
