@@ -17,7 +17,8 @@
  *    example torch tensors' data_ptr()); "host" pointers are ordinary memory.
  *  - The caller owns every buffer.  The library allocates nothing on the
  *    device and keeps no mutable global state, so calls on different streams
- *    are independent.
+ *    are independent.  The one exception is nvfp4_moe_forward_noalloc, whose
+ *    workspace is a fixed static buffer per device (see there).
  *  - Calls that take a stream only enqueue work on it (NULL = the default
  *    stream) and never synchronise the host.  A launch failure reported by the
  *    HIP runtime returns NVFP4_ERR_DEVICE; argument problems found on the host
@@ -55,7 +56,8 @@ typedef enum {
   NVFP4_ERR_BAD_SCALE = 2,    /* a per-expert input scale failed the load check */
   NVFP4_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required     */
   NVFP4_ERR_DEVICE = 4,       /* the HIP runtime reported an error              */
-  NVFP4_ERR_UNSUPPORTED = 5   /* valid request outside the built kernels' shapes */
+  NVFP4_ERR_UNSUPPORTED = 5,  /* valid request outside the built kernels' shapes */
+  NVFP4_ERR_TOO_LARGE = 6     /* needs more than nvfp4_moe_forward_noalloc's fixed buffer */
 } nvfp4_status_t;
 
 /* Per-slot verdicts of nvfp4_validate_scales. */
@@ -73,7 +75,7 @@ NVFP4_API const char* nvfp4_status_string(nvfp4_status_t status);
 
 /* ABI revision of this header; bumped on any incompatible change. */
 NVFP4_API int32_t nvfp4_abi_version(void);
-#define NVFP4_ABI_VERSION 4
+#define NVFP4_ABI_VERSION 5
 
 /*
  * nvfp4_validate_scales — the load-time completeness check (page 3, "ROOT
@@ -356,6 +358,32 @@ NVFP4_API nvfp4_status_t nvfp4_moe_forward(const nvfp4_moe_weights_t* w, const v
                                            int32_t k, const void* residual_bf16, void* out_bf16,
                                            void* workspace, size_t workspace_bytes,
                                            const nvfp4_moe_debug_t* debug, nvfp4_stream_t stream);
+
+/*
+ * nvfp4_moe_forward_noalloc — nvfp4_moe_forward for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid hipMalloc.  The same layer, arguments, results,
+ * debug buffers and errors as nvfp4_moe_forward, without the workspace
+ * arguments: the workspace is a fixed buffer of NVFP4_NOALLOC_SCRATCH_BYTES
+ * in static device memory that the library holds on every device it runs on
+ * until the process ends.  Nothing is allocated or freed.
+ *   Runs on the current device; `stream` must belong to it.
+ *   Returns NVFP4_ERR_TOO_LARGE, before anything is enqueued, when
+ *   nvfp4_moe_workspace_size(num_tokens, k, w) exceeds the buffer (at hidden
+ *   2816, intermediate 704 and top-8: about 600 tokens).
+ *   Every call on one device shares that device's buffer, which keeps the
+ *   last call's contents: calls that overlap in time on one device (on two
+ *   streams, or from two host threads) race, and the caller must serialise
+ *   them.  No part of the buffer needs to start at zero.
+ */
+#define NVFP4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+NVFP4_API nvfp4_status_t nvfp4_moe_forward_noalloc(const nvfp4_moe_weights_t* w,
+                                                   const void* x_bf16,
+                                                   const float* router_logits,
+                                                   int32_t num_tokens, int32_t k,
+                                                   const void* residual_bf16, void* out_bf16,
+                                                   const nvfp4_moe_debug_t* debug,
+                                                   nvfp4_stream_t stream);
 
 /*
  * Weight-only (W4A16) forward of the same layer (page 3, "Kernel Backend" and

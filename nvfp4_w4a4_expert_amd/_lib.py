@@ -18,7 +18,9 @@ import numpy as np
 
 from .build import LIB_PATH
 
-OK, ERR_INVALID_ARG, ERR_BAD_SCALE, ERR_WORKSPACE, ERR_DEVICE, ERR_UNSUPPORTED = range(6)
+(OK, ERR_INVALID_ARG, ERR_BAD_SCALE, ERR_WORKSPACE, ERR_DEVICE, ERR_UNSUPPORTED,
+ ERR_TOO_LARGE) = range(7)
+NOALLOC_SCRATCH_BYTES = 64 << 20      # NVFP4_NOALLOC_SCRATCH_BYTES
 SLOT_OK, SLOT_UNWRITTEN, SLOT_NAN, SLOT_INF, SLOT_NONPOSITIVE, SLOT_RECIP_OVERFLOW = range(6)
 
 if not os.path.exists(LIB_PATH):
@@ -76,6 +78,8 @@ _SIGS = {
                                               ctypes.POINTER(ctypes.c_size_t)]),
     "nvfp4_moe_forward_w4a16": (_i32, [ctypes.POINTER(MoEWeights), _p, _p, _i32, _i32, _p, _p,
                                        _p, ctypes.c_size_t, ctypes.POINTER(MoEDebug), _p]),
+    "nvfp4_moe_forward_noalloc": (_i32, [ctypes.POINTER(MoEWeights), _p, _p, _i32, _i32, _p, _p,
+                                         ctypes.POINTER(MoEDebug), _p]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -245,3 +249,11 @@ def moe_forward_mx(weights: MoEWeights, x, router_logits, num_tokens: int, k: in
                                      num_tokens, k, _ptr(residual), _ptr(out), _ptr(workspace),
                                      workspace_bytes, None if debug is None else ctypes.byref(debug),
                                      _stream(stream)), "nvfp4_moe_forward_mx")
+
+
+def moe_forward_noalloc(weights: MoEWeights, x, router_logits, num_tokens: int, k: int, residual,
+                        out, debug: Optional[MoEDebug] = None, stream=None):
+    _check(_lib.nvfp4_moe_forward_noalloc(ctypes.byref(weights), _ptr(x), _ptr(router_logits),
+                                          num_tokens, k, _ptr(residual), _ptr(out),
+                                          None if debug is None else ctypes.byref(debug),
+                                          _stream(stream)), "nvfp4_moe_forward_noalloc")

@@ -21,7 +21,7 @@ LIB_NAME = "libnvfp4moe.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "quant.hip", "route.hip", "gemm.hip", "combine.hip"]
+SOURCES = ["api.cpp", "quant.hip", "route.hip", "gemm.hip", "combine.hip", "noalloc.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

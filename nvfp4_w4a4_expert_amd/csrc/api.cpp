@@ -84,6 +84,8 @@ NVFP4_API const char* nvfp4_status_string(nvfp4_status_t status) {
     case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
     case NVFP4_ERR_DEVICE: return "HIP runtime error";
     case NVFP4_ERR_UNSUPPORTED: return "shape not supported by the built kernels";
+    case NVFP4_ERR_TOO_LARGE:
+      return "request needs more workspace than the allocation-free forward's fixed buffer";
   }
   return "unknown status";
 }

@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
                  "nvfp4_quantize_experts_fp16", "nvfp4_calibrate_input_scales",
                  "nvfp4_moe_forward_w4a16", "nvfp4_moe_workspace_size_w4a16",
                  "nvfp4_quantize_experts_mx", "nvfp4_moe_pack_weights_mx",
-                 "nvfp4_moe_forward_mx"]:
+                 "nvfp4_moe_forward_mx", "nvfp4_moe_forward_noalloc"]:
         assert name in syms
 
 
@@ -49,8 +49,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = _lib()
-    assert L.abi_version() == 4
-    for s in range(6):
+    assert L.abi_version() == 5
+    for s in range(7):
         assert L.status_string(s)
     assert "unknown" in L.status_string(99)
 
@@ -210,3 +210,23 @@ def test_bad_scales_are_rejected_before_upload():
         M.NVFP4MoELayer(None, None, None, None, None, None, np.ones(w.E), np.ones(w.E),
                         written13=None, written2=wr, device="meta")
     assert ei.value.bad_slots == [1] and ei.value.projection == "w2"
+
+
+def test_noalloc_forward_rejects_before_touching_the_device():
+    """The allocation-free forward checks its arguments and the size of its
+    fixed buffer on the host before any HIP call."""
+    L = _lib()
+    f = L._lib
+    w = L.MoEWeights()
+    assert f.nvfp4_moe_forward_noalloc(ctypes.byref(w), None, None, 4, 2, None, None, None,
+                                       None) == L.ERR_INVALID_ARG
+    assert f.nvfp4_moe_forward_noalloc(None, None, None, 4, 2, None, None, None,
+                                       None) == L.ERR_INVALID_ARG
+    fake = 4096
+    w = L.MoEWeights(*([fake] * 10), 128, 2816, 704)
+    need = L.moe_workspace_size(1024, 8, w)
+    assert need > L.NOALLOC_SCRATCH_BYTES
+    assert f.nvfp4_moe_forward_noalloc(ctypes.byref(w), fake, fake, 1024, 8, None, fake, None,
+                                       None) == L.ERR_TOO_LARGE
+    assert L.moe_workspace_size(512, 8, w) <= L.NOALLOC_SCRATCH_BYTES
+    assert "fixed buffer" in L.status_string(L.ERR_TOO_LARGE)
