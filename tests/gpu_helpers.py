@@ -35,19 +35,98 @@ def bf16_f64(bits):
     return OF.bf16_to_f32(bits).astype(np.float64)
 
 
-def assert_correctly_rounded_bf16(got, exact, label):
-    """Every bf16 element is within half an ulp of the exact value (|exact| *
-    2^-8 bounds half an ulp, 1% slack for the fp32 computation before the
-    rounding) plus an absolute floor of 2^-16 of the row's RMS that covers
-    fp32 cancellation in sums whose result is much smaller than their terms."""
+U32 = 2.0 ** -24          # unit roundoff of fp32 (round to nearest)
+
+
+def bf16_half_ulp(v):
+    """Half the spacing of bf16 numbers at |v|.  bf16 keeps 8 significant
+    bits, so in the binade [2^e, 2^(e+1)) the spacing is 2^(e-7) and half of
+    it 2^(e-8); below 2^-126 the spacing stays 2^-133."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return np.ldexp(1.0, (e - 8).astype(np.int64))
+
+
+def assert_correctly_rounded_bf16(got, exact, err32, label):
+    """Every bf16 element is the nearest bf16 number to a value that lies
+    within err32 of the exact (fp64) one, where err32 bounds the GPU's fp32
+    error before its single rounding to bf16:
+        |got - exact| <= half_ulp(|exact| + err32) + err32."""
     got = np.asarray(got, dtype=np.float64)
     exact = np.asarray(exact, dtype=np.float64)
-    rms = np.sqrt(np.mean(exact * exact, axis=1, keepdims=True))
-    bound = np.abs(exact) * 2.0 ** -8 * 1.01 + rms * 2.0 ** -16
+    err32 = np.asarray(err32, dtype=np.float64)
+    bound = bf16_half_ulp(np.abs(exact) + err32) + err32
     err = np.abs(got - exact)
     bad = err > bound
-    assert not bad.any(), (label, "elements outside half a bf16 ulp", int(bad.sum()),
-                           float((err / np.maximum(bound, 1e-300)).max()))
+    assert not bad.any(), (label, "elements beyond half a bf16 ulp + the fp32 error bound",
+                           int(bad.sum()), float((err / np.maximum(bound, 1e-300)).max()))
+
+
+def dot_error_bound(a_norm, w_norm, alpha, row_expert, K):
+    """Bound on the fp32 error of the GPU's grouped-GEMM outputs
+    C[p, n] = alpha[e] * sum_k A[p, k] W[e][n, k] (exact operands, fp32
+    accumulation): |fl(C) - C| <= gamma * u * |alpha| * sum_k |A W| with
+    gamma = K/16 + 64 (one rounding per accumulation step of a 16-deep matrix
+    instruction, plus a budget of 64 for the instruction's internal sum and the
+    product by alpha; a 64-deep instruction needs fewer steps), and
+    sum_k |A W| <= ||A[p]|| ||W[e][n]|| (Cauchy-Schwarz).  a_norm [P],
+    w_norm [E, N] -> [P, N]."""
+    gamma = K / 16 + 64
+    e = np.asarray(row_expert, dtype=np.int64)
+    scale = gamma * U32 * np.abs(np.asarray(alpha, dtype=np.float64))[e] * a_norm
+    return scale[:, None] * w_norm[e]
+
+
+def weight_row_norms(layer, proj: str, dequant):
+    """||dequantised W[e][n]|| for every expert e and weight row n (cached on
+    the layer)."""
+    key = f"_norms_{proj}"
+    if not hasattr(layer, key):
+        codes, sf = (layer.w13c, layer.w13s) if proj == "w13" else (layer.w2c, layer.w2s)
+        setattr(layer, key, np.stack([np.linalg.norm(dequant(codes[e], sf[e]), axis=1)
+                                      for e in range(codes.shape[0])]))
+    return getattr(layer, key)
+
+
+def routing_weight_bound(logits, ids, w_ref):
+    """Bound on the GPU's fp32 softmax weights against the fp64 ones.  With
+    d_j = l_j - l_max (rounded once in fp32), exp correct to an ulp, k - 1
+    additions and one division, the relative error of weight j is at most
+    (|d_j| + max_i |d_i| + k + 8) u."""
+    sel = np.take_along_axis(np.asarray(logits, dtype=np.float64),
+                             np.asarray(ids, dtype=np.int64), axis=1)
+    d = np.abs(sel - sel[:, :1])
+    k = sel.shape[1]
+    return np.abs(w_ref) * U32 * (d + d.max(axis=1, keepdims=True) + k + 8)
+
+
+def silu_mul_error_bound(c1_exact, err_c1, I):
+    """Bound on the fp32 error of h = silu(gate) * up computed from fp32 C1
+    values that are each within err_c1 of c1_exact: |dsilu/dg| <= 1.1
+    carries the gate's error, |silu(g)| the up's, and the fp32 evaluation
+    itself (exp of an argument rounded to fp32, a reciprocal and two
+    products) adds (|g| + 16) u of |h|."""
+    g, u = c1_exact[:, :I], c1_exact[:, I:2 * I]
+    dg, du = err_c1[:, :I], err_c1[:, I:2 * I]
+    with np.errstate(over="ignore"):
+        s = g / (1.0 + np.exp(-g))
+    return 1.1 * np.abs(u) * dg + np.abs(s) * du + (np.abs(g) + 16.0) * U32 * np.abs(s * u)
+
+
+def combine_error_bound(c2_exact, err_c2, w_ref, w_err, inv, T, k, residual_f32=None):
+    """Bound on the fp32 error of out[t] = residual[t] + sum_j w[t,j] C2[q]
+    before its rounding to bf16: the C2 rows' own errors weighted, the
+    routing weights' errors times |C2|, and k + 2 roundings of the running
+    sum."""
+    invm = np.asarray(inv).reshape(T, k)
+    err = np.zeros((T, c2_exact.shape[1]))
+    mag = np.zeros_like(err) if residual_f32 is None else np.abs(residual_f32).astype(np.float64)
+    for j in range(k):
+        rows = invm[:, j]
+        a = np.abs(c2_exact[rows])
+        err += np.abs(w_ref[:, j:j + 1]) * err_c2[rows] + w_err[:, j:j + 1] * a
+        mag += np.abs(w_ref[:, j:j + 1]) * a
+    return err + (k + 2) * U32 * mag
 
 
 @functools.lru_cache(maxsize=4)
@@ -137,11 +216,14 @@ def check_layer_parity(layer: OM.Layer, x_bits, logits, k, residual_bits=None, l
     Unique results are compared exactly (routing ids, permutation, A1 codes
     and scales).  Floating-point stages are compared per row within
     REL_L2_TOL against the fp64 reference over the same dequantised
-    operands.  A2 depends on h's rounding, so it is checked to be the oracle
+    operands, and element by element: h and the output must be the bf16
+    rounding of a value within the fp32 error bound of the exact one (half a
+    bf16 ulp plus that bound); routing weights within the fp32 softmax
+    bound.  A2 depends on h's rounding, so it is checked to be the oracle
     quantiser's image of the GPU's own h, and GEMM2 is referenced over that
     A2.  Returns a dict of summary metrics."""
     T = x_bits.shape[0]
-    E, I = layer.E, layer.I
+    E, I, H = layer.E, layer.I, layer.H
     progress(f"{label}: GPU forward")
     got = run_forward(layer, x_bits, logits, k, residual_bits, mx=mx)
     progress(f"{label}: oracle forward")
@@ -150,24 +232,29 @@ def check_layer_parity(layer: OM.Layer, x_bits, logits, k, residual_bits=None, l
     progress(f"{label}: comparing")
 
     assert np.array_equal(got["topk_ids"], ref["ids"]), label + " routing ids"
-    wrel = np.abs(got["topk_weights"] - ref["w"]) / np.abs(ref["w"])
-    assert wrel.max() < 2e-6, (label, "routing weights", wrel.max())
+    w_err = routing_weight_bound(logits, ref["ids"], ref["w"])
+    assert np.all(np.abs(got["topk_weights"] - ref["w"]) <= w_err), (
+        label, "routing weights", float((np.abs(got["topk_weights"] - ref["w"]) / w_err).max()))
     assert np.array_equal(got["expert_offsets"], ref["offsets"]), label + " offsets"
     assert np.array_equal(got["src_pair"], ref["src_pair"]), label + " src_pair"
     assert np.array_equal(got["inv_pair"], ref["inv"]), label + " inv_pair"
     assert np.array_equal(got["a1_codes"], ref["a1"][0]), label + " A1 codes"
     assert np.array_equal(got["a1_sf"], ref["a1"][1]), label + " A1 scales"
 
+    rexp = OM.row_experts(ref["offsets"])
     c1 = rel_l2_rows(got["c1"], ref["c1"])
     assert c1.max() <= REL_L2_TOL, (label, "C1", c1.max())
-    # h is bf16: the GPU rounds its fp32 SiLU*mul once, so every element is
-    # within half a bf16 ulp of the fp64 value, up to fp32 error (floor).
+    a1_norm = np.linalg.norm(OQm.dequant(*ref["a1"]), axis=1)
+    err_c1 = dot_error_bound(a1_norm, weight_row_norms(layer, "w13", OQm.dequant), layer.alpha1,
+                             rexp, H)
+    assert np.all(np.abs(got["c1"] - ref["c1"]) <= err_c1), (label, "C1 elements")
     h_exact = OM.silu_mul(ref["c1"], I)
     h_gpu = bf16_f64(got["h"])
-    assert_correctly_rounded_bf16(h_gpu, h_exact, label + " h")
+    assert_correctly_rounded_bf16(h_gpu, h_exact, silu_mul_error_bound(ref["c1"], err_c1, I),
+                                  label + " h")
     hr = rel_l2_rows(h_gpu, h_exact)
+    del err_c1
 
-    rexp = OM.row_experts(ref["offsets"])
     a2c, a2s = OQm.quantize_experts(got["h"], rexp, ref["a2_gscale"])
     assert np.array_equal(got["a2_codes"], a2c), label + " A2 codes vs Q(h_gpu)"
     assert np.array_equal(got["a2_sf"], a2s), label + " A2 scales vs Q(h_gpu)"
@@ -177,11 +264,17 @@ def check_layer_parity(layer: OM.Layer, x_bits, logits, k, residual_bits=None, l
                                                  layer.w2c, layer.w2s, layer.alpha2)
     c2 = rel_l2_rows(got["c2"], c2_ref)
     assert c2.max() <= REL_L2_TOL, (label, "C2", c2.max())
+    a2_norm = np.linalg.norm(OQm.dequant(got["a2_codes"], got["a2_sf"]), axis=1)
+    err_c2 = dot_error_bound(a2_norm, weight_row_norms(layer, "w2", OQm.dequant), layer.alpha2,
+                             rexp, I)
+    assert np.all(np.abs(got["c2"] - c2_ref) <= err_c2), (label, "C2 elements")
 
     res = None if residual_bits is None else OF.bf16_to_f32(residual_bits)
     out_ref = OM.combine_ref(c2_ref, ref["w"], ref["inv"], T, k, res)
     out_gpu = bf16_f64(got["out"])
-    assert_correctly_rounded_bf16(out_gpu, out_ref, label + " out")
+    err_out = combine_error_bound(c2_ref, err_c2, ref["w"], w_err, ref["inv"], T, k, res)
+    del err_c2
+    assert_correctly_rounded_bf16(out_gpu, out_ref, err_out, label + " out")
     outr = rel_l2_rows(out_gpu, out_ref)
     out_vs_rounded = rel_l2_rows(out_gpu, bf16_f64(OF.f64_to_bf16(out_ref)))
     assert out_vs_rounded.max() <= REL_L2_TOL, (label, "out vs bf16(ref)", out_vs_rounded.max())
@@ -198,13 +291,14 @@ def check_layer_parity(layer: OM.Layer, x_bits, logits, k, residual_bits=None, l
 def check_layer_parity_w4a16(layer: OM.Layer, x_bits, logits, k, residual_bits=None, label=""):
     """Stage-by-stage parity of one weight-only (W4A16) GPU forward against
     the oracle's layer_forward_w4a16.  Routing and permutation exactly; C1
-    per row within REL_L2_TOL of the fp64 product of the bf16 x rows and the
-    dequantised weights; h correctly rounded from the fp64 SiLU*mul; C2
-    against the fp64 product over the GPU's own h (one bf16 rounding may
-    differ from the oracle's); the output correctly rounded from that C2's
-    combine."""
+    per row within REL_L2_TOL (and element by element within the fp32
+    accumulation bound) of the fp64 product of the bf16 x rows and the
+    dequantised weights; h the bf16 rounding of a value within the fp32 bound
+    of the fp64 SiLU*mul; C2 against the fp64 product over the GPU's own h
+    (one bf16 rounding may differ from the oracle's); the output likewise
+    from that C2's combine."""
     T = x_bits.shape[0]
-    I = layer.I
+    I, H = layer.I, layer.H
     progress(f"{label}: GPU W4A16 forward")
     got = run_forward(layer, x_bits, logits, k, residual_bits, w4a16=True)
     progress(f"{label}: oracle W4A16 forward")
@@ -212,29 +306,41 @@ def check_layer_parity_w4a16(layer: OM.Layer, x_bits, logits, k, residual_bits=N
     progress(f"{label}: comparing")
 
     assert np.array_equal(got["topk_ids"], ref["ids"]), label + " routing ids"
-    wrel = np.abs(got["topk_weights"] - ref["w"]) / np.abs(ref["w"])
-    assert wrel.max() < 2e-6, (label, "routing weights", wrel.max())
+    w_err = routing_weight_bound(logits, ref["ids"], ref["w"])
+    assert np.all(np.abs(got["topk_weights"] - ref["w"]) <= w_err), (label, "routing weights")
     assert np.array_equal(got["expert_offsets"], ref["offsets"]), label + " offsets"
     assert np.array_equal(got["src_pair"], ref["src_pair"]), label + " src_pair"
     assert np.array_equal(got["inv_pair"], ref["inv"]), label + " inv_pair"
 
+    rexp = OM.row_experts(ref["offsets"])
     c1 = rel_l2_rows(got["c1"], ref["c1"])
     assert c1.max() <= REL_L2_TOL, (label, "C1", c1.max())
+    x_norm = np.linalg.norm(bf16_f64(np.asarray(x_bits)[ref["src_pair"] // k]), axis=1)
+    err_c1 = dot_error_bound(x_norm, weight_row_norms(layer, "w13", OQ.dequant), layer.w13s2,
+                             rexp, H)
+    assert np.all(np.abs(got["c1"] - ref["c1"]) <= err_c1), (label, "C1 elements")
     h_exact = OM.silu_mul(ref["c1"], I)
     h_gpu = bf16_f64(got["h"])
-    assert_correctly_rounded_bf16(h_gpu, h_exact, label + " h")
+    assert_correctly_rounded_bf16(h_gpu, h_exact, silu_mul_error_bound(ref["c1"], err_c1, I),
+                                  label + " h")
     hr = rel_l2_rows(h_gpu, h_exact)
+    del err_c1
 
     progress(f"{label}: oracle W4A16 GEMM2 over the GPU's h")
     c2_ref = OM.grouped_gemm_w16_ref(OF.bf16_to_f32(got["h"]), ref["offsets"], layer.w2c,
                                      layer.w2s, layer.w2s2)
     c2 = rel_l2_rows(got["c2"], c2_ref)
     assert c2.max() <= REL_L2_TOL, (label, "C2", c2.max())
+    err_c2 = dot_error_bound(np.linalg.norm(h_gpu, axis=1),
+                             weight_row_norms(layer, "w2", OQ.dequant), layer.w2s2, rexp, I)
+    assert np.all(np.abs(got["c2"] - c2_ref) <= err_c2), (label, "C2 elements")
 
     res = None if residual_bits is None else OF.bf16_to_f32(residual_bits)
     out_ref = OM.combine_ref(c2_ref, ref["w"], ref["inv"], T, k, res)
     out_gpu = bf16_f64(got["out"])
-    assert_correctly_rounded_bf16(out_gpu, out_ref, label + " out")
+    err_out = combine_error_bound(c2_ref, err_c2, ref["w"], w_err, ref["inv"], T, k, res)
+    del err_c2
+    assert_correctly_rounded_bf16(out_gpu, out_ref, err_out, label + " out")
     outr = rel_l2_rows(out_gpu, out_ref)
     e2e = rel_l2_rows(out_gpu, ref["out_f64"])
     h_diffs = int(np.count_nonzero(got["h"] != ref["h_bits"]))

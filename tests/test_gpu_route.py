@@ -1,5 +1,5 @@
-"""GPU parity of the router (top-k ids bit-exact, softmax weights to fp32
-accuracy) and of the stable permutation (offsets, src_pair, inv bit-exact)
+"""GPU parity of the router (top-k ids bit-exact, softmax weights within the
+fp32 error bound of the fp64 softmax) and of the stable permutation (offsets, src_pair, inv bit-exact)
 on every workload's router law, including tie-heavy logits and Zipf routing
 that leaves experts without tokens."""
 import numpy as np
@@ -7,6 +7,8 @@ import pytest
 
 import synthetic as S
 from oracle import moe as OM
+
+from gpu_helpers import routing_weight_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +35,8 @@ def _check(logits, k):
     roff, rsrc, rinv = OM.permute(rids, logits.shape[1])
     assert np.array_equal(ids, rids)
     err = np.abs(w - rw)
-    assert np.all(err <= 2e-6 * np.abs(rw)), (err / np.maximum(np.abs(rw), 1e-300)).max()
+    bound = routing_weight_bound(logits, rids, rw)
+    assert np.all(err <= bound), (err / bound).max()
     assert np.array_equal(off, roff)
     assert np.array_equal(src, rsrc)
     assert np.array_equal(inv, rinv)
