@@ -69,6 +69,7 @@
 // instruction; GEMM1 requantises h in the UE8M0 mode.
 #include <type_traits>
 
+#include "gemm_tiles.h"
 #include "internal.h"
 #include "nvfp4_device.h"
 
@@ -83,42 +84,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-// Operand modes of the grouped GEMM.
-constexpr int kModeNV = 0;     // NVFP4 x NVFP4, fp16 MFMA on exact dequantised values
-constexpr int kModeW16 = 1;    // bf16 activations x NVFP4 weights, bf16 MFMA
-constexpr int kModeMX = 2;     // UE8M0 FP4 x UE8M0 FP4, scaled FP4 MFMA
-
-constexpr int kXcds = 8;
-
-// Launch shapes for batches with at least 32 rows per expert on average
-// (chosen by measurement on MI355X at the 4096-token prefill layer):
-//   w13: 8 wavefronts (256 h columns), 64-row tiles, K step 128, 3-slot
-//        register rings, one workgroup per CU: the staged token tile serves
-//        twice the weight columns of a 4-wavefront workgroup
-//   w2:  4 wavefronts (256 output columns), 128-row tiles, K step 64, 2-slot
-//        register rings, 2 workgroups per CU
-// (two wavefronts per SIMD, at most 256 VGPRs per lane; 96- or 128-row w13
-// tiles either do not fit with 3-slot rings or lose more to latency with
-// 2-slot rings than they save in dequantisation.)
-constexpr int kG1Waves = 8, kG1MB = 2, kG1BK = 128, kG1Ring = 3, kG1Occ = 1;
-// UE8M0 mode w13: K step 256 (nothing to dequantise, so a 128-wide step is
-// too little matrix work per barrier and per prefetch slot); 96-row tiles
-// with a 2-slot register ring, which reuse each weight fragment over a third
-// more rows for the same registers as 64-row tiles with 3 slots (measured
-// 140 -> 129 us at the prefill layer)
-constexpr int kG1BKmx = 256, kG1MBmx = 3, kG1RingMx = 2;
-// weight-only mode w13: 96-row tiles with a 2-slot ring as well (its weights
-// cost twice the dequantisation instructions of the E4M3 mode, so reusing each
-// fragment over more rows pays: measured 342 -> 321 us at the prefill layer)
-constexpr int kG1MBw16 = 3, kG1RingW16 = 2;
-constexpr int kG2MB = 4, kG2Ring = 2, kG2Occ = 2;
-// UE8M0 mode w2: 3 ring slots (no dequantisation registers, so the deeper
-// ring fits in 247 VGPRs; measured 138 -> 136 us; in the other modes it spills)
-constexpr int kG2RingMx = 3;
-// Batches with fewer than 32 rows per expert on average (decode): one 32-row
-// sub-tile, 4 wavefronts, 2 workgroups per CU; ring depth for w13 / w2.
-constexpr int kS1Ring = 3, kS2Ring = 3;
-constexpr int kMaxExperts = 1024;
+// Launch shapes, operand modes, tile mapping and global address arithmetic
+// live in gemm_tiles.h, shared with the host-side range checker.
+using namespace gemm_map;
 
 template <int V>
 using Int = std::integral_constant<int, V>;
@@ -272,31 +240,19 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
   }
   const int32_t total_m = s_mt[prm.E];
   const int32_t total = total_m * prm.n_tiles;
-  const int32_t per_xcd = (total + kXcds - 1) / kXcds;
+  const int32_t xcd_tiles = per_xcd(total);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5;
   const int32_t K = prm.K;
-  const int64_t kb2 = K / 2, kb16 = K / 16, kb32 = K / 32;
   const int nk = K / kBK;
 
   // ---- persistent loop over tiles; the workgroups on one XCD walk a
   // contiguous range of (m-tile, n-tile) so they share that XCD's L2 --------
-  for (int32_t t = blockIdx.x; t < per_xcd * kXcds; t += gridDim.x) {
-  const int32_t logical = (t % kXcds) * per_xcd + t / kXcds;
+  for (int32_t t = blockIdx.x; t < xcd_tiles * kXcds; t += gridDim.x) {
+  const int32_t logical = logical_tile(t, xcd_tiles);
   if (logical >= total) continue;
-  const int32_t mt = logical / prm.n_tiles;
-  const int32_t nt = logical - mt * prm.n_tiles;
-  int32_t e = 0;
-  {
-    int32_t lo = 0, hi = prm.E - 1;                      // last e with s_mt[e] <= mt
-    while (lo < hi) {
-      const int32_t mid = (lo + hi + 1) >> 1;
-      if (s_mt[mid] <= mt) lo = mid; else hi = mid - 1;
-    }
-    e = lo;
-  }
-  const int32_t row0 = s_off[e] + (mt - s_mt[e]) * kBM;
-  const int32_t rows = min(kBM, s_off[e + 1] - row0);
+  const Tile tl = tile_of(logical, prm.n_tiles, s_mt, s_off, prm.E, kBM);
+  const int32_t nt = tl.nt, e = tl.e, row0 = tl.row0, rows = tl.rows;
   if (rows <= 0) continue;                             // (uniform; never for consistent offsets)
 
   // ---- B streaming assignment: wave's 64 weight rows, 2 blocks of 32 ------
@@ -305,23 +261,17 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
   // K step kt holds, lane by lane, the 16-byte pieces each lane consumes, so a
   // wavefront's load is one contiguous 1 KB per piece (plus 64 contiguous
   // scale groups of kBK/32 bytes).
-  const int32_t hc0 = kGated ? nt * (32 * kWaves) + 32 * wave : 0;   // h column base
-  const int32_t n0 = kGated ? 0 : nt * (64 * kWaves) + 64 * wave;    // output column base
-  const bool active = kGated ? hc0 < prm.I : n0 < prm.N_w;
+  const WaveBlocks wb = wave_blocks(kGated, kWaves, nt, wave, prm.I, prm.N_w);
+  const int32_t n0 = wb.n0;                            // GEMM2: output column base
+  const bool active = wb.active;                       // inactive waves read block 0
   const uint8_t* b_cp[2];
   const uint8_t* b_sp[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    int32_t blk_row0;                                  // first row of the 32-row block
-    if (kGated) blk_row0 = j == 0 ? hc0 : prm.I + hc0;
-    else blk_row0 = n0 + 32 * j;
-    if (!active) blk_row0 = 0;                         // inactive waves read block 0
-    const int64_t rbase = (int64_t)e * prm.N_w + blk_row0;
-    b_cp[j] = prm.w_codes + rbase * kb2 + 16 * lane;
+    b_cp[j] = prm.w_codes + b_codes_offset(e, prm.N_w, wb.row0[j], K, lane);
     // scale bytes per lane per K step: kBK/32 E4M3 scales (16-element
     // blocks) or kBK/64 UE8M0 scales (32-element blocks)
-    b_sp[j] = kMX ? prm.w_sf + rbase * kb32 + (kBK / 64) * lane
-                  : prm.w_sf + rbase * kb16 + (kBK / 32) * lane;
+    b_sp[j] = prm.w_sf + b_scales_offset(e, prm.N_w, wb.row0[j], K, lane, kBK, kMX);
   }
 
   // The tile body, for kMBa = the number of 32-row sub-tiles that hold rows
@@ -333,7 +283,7 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
   // 16 elements when that is what it takes to give every thread a chunk;
   // bf16 rows (kW16) in chunks of 8 elements (16 bytes); UE8M0 codes (kMX) in
   // chunks of one 32-element block (16 code bytes + 1 scale byte).
-  constexpr int kCE = kW16 ? 8 : kMX ? 32 : 32 * kMBa * (kBK / 32) >= kThreads ? 32 : 16;
+  constexpr int kCE = a_chunk_elems(kMode, kMBa, kBK, kThreads);
   constexpr int kCPR = kBK / kCE;                        // chunks per row per step
   constexpr int kChunks = 32 * kMBa * kCPR;
   constexpr int kChunksPerThread = (kChunks + kThreads - 1) / kThreads;
@@ -352,17 +302,14 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
     a_on[i] = kChunks % kThreads == 0 || c < kChunks;   // compile-time true when exact
     const int cc = a_on[i] ? c : 0;
     const int r = cc / kCPR, kc = cc % kCPR;
-    const int64_t arow = row0 + min(r, rows - 1);
+    const int64_t arow = a_row(row0, r, rows);
     if constexpr (kW16) {
       const int64_t srow = prm.a_src ? prm.a_src[arow] / prm.a_src_div : arow;
-      a_cp[i] = reinterpret_cast<const uint8_t*>(prm.a_rows + srow * prm.lda + kCE * kc);
+      a_cp[i] = reinterpret_cast<const uint8_t*>(prm.a_rows + a_rows_offset(srow, prm.lda, kc, kCE));
       a_sp[i] = nullptr;
-    } else if constexpr (kMX) {
-      a_cp[i] = prm.a_codes + arow * kb2 + 16 * kc;
-      a_sp[i] = prm.a_sf + arow * kb32 + kc;
     } else {
-      a_cp[i] = prm.a_codes + arow * kb2 + (kCE / 2) * kc;
-      a_sp[i] = prm.a_sf + arow * kb16 + (kCE / 16) * kc;
+      a_cp[i] = prm.a_codes + a_codes_offset(arow, K, kc, kCE, kMX);
+      a_sp[i] = prm.a_sf + a_scales_offset(arow, K, kc, kCE, kMX);
     }
     a_lds[i] = kMX ? r * kLdAb + 16 * kc : r * kLdA + kCE * kc;
     a_lds_s[i] = kScOff + r * (kBK / 32) + kc;
@@ -387,16 +334,16 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
     for (int i = 0; i < kChunksPerThread; ++i) {
       if (!a_on[i]) continue;
       if constexpr (kW16) {
-        a_raw[slot][i] = *reinterpret_cast<const araw_t*>(a_cp[i] + (int64_t)kt * (kBK * 2));
+        a_raw[slot][i] = *reinterpret_cast<const araw_t*>(a_cp[i] + 2 * a_rows_step(kt, kBK));
         continue;
       }
-      a_raw[slot][i] = *reinterpret_cast<const araw_t*>(a_cp[i] + (int64_t)kt * (kBK / 2));
+      a_raw[slot][i] = *reinterpret_cast<const araw_t*>(a_cp[i] + a_codes_step(kt, kBK));
       if constexpr (kMX)
-        a_sraw[slot][i] = a_sp[i][(int64_t)kt * (kBK / 32)];
+        a_sraw[slot][i] = a_sp[i][a_scales_step(kt, kBK, true)];
       else if constexpr (kCE == 32)
-        a_sraw[slot][i] = *reinterpret_cast<const uint16_t*>(a_sp[i] + (int64_t)kt * (kBK / 16));
+        a_sraw[slot][i] = *reinterpret_cast<const uint16_t*>(a_sp[i] + a_scales_step(kt, kBK, false));
       else
-        a_sraw[slot][i] = a_sp[i][(int64_t)kt * (kBK / 16)];
+        a_sraw[slot][i] = a_sp[i][a_scales_step(kt, kBK, false)];
     }
   };
   // dequantise the A step held in register slot `slot` into LDS buffer `buf`
@@ -432,17 +379,17 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
     constexpr int buf = decltype(slotc)::value;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const uint8_t* cbase = b_cp[j] + (int64_t)kt * (kVec * 1024);
+      const uint8_t* cbase = b_cp[j] + b_codes_step(kt, kBK);
 #pragma unroll
       for (int v = 0; v < kVec; ++v)
         b_raw[buf][j][v] = *reinterpret_cast<const u32x4*>(cbase + 1024 * v);
       if constexpr (kMX) {
-        const uint8_t* sp = b_sp[j] + (int64_t)kt * (64 * (kBK / 64));
+        const uint8_t* sp = b_sp[j] + b_scales_step(kt, kBK, true);
         if constexpr (kBK == 256) b_sraw[buf][j] = *reinterpret_cast<const uint32_t*>(sp);
         else if constexpr (kBK == 128) b_sraw[buf][j] = *reinterpret_cast<const uint16_t*>(sp);
         else b_sraw[buf][j] = *sp;
       } else {
-        const uint8_t* sp = b_sp[j] + (int64_t)kt * (64 * (kBK / 32));
+        const uint8_t* sp = b_sp[j] + b_scales_step(kt, kBK, false);
         if constexpr (kBK == 128) b_sraw[buf][j] = *reinterpret_cast<const uint32_t*>(sp);
         else b_sraw[buf][j] = *reinterpret_cast<const uint16_t*>(sp);
       }
@@ -641,7 +588,7 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
       // it (where they would stay live across the loop).
       const int32_t ldc = opaque_sgpr(prm.ldc);
       const int32_t r0 = opaque_sgpr(row0);
-      float* gout = prm.c_out + (int64_t)r0 * ldc + n0 + c4;
+      float* gout = prm.c_out + c_offset(r0, 0, ldc, n0, c4);
       if (active)
 #pragma unroll
       for (int mi = 0; mi < kMBa; ++mi) {
@@ -698,10 +645,10 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
           if (row < rows) {
             const int64_t p = row0 + row;
             if (prm.c1_dbg) {
-              prm.c1_dbg[p * 2 * I + hbase + col] = gv;
-              prm.c1_dbg[p * 2 * I + I + hbase + col] = uv;
+              prm.c1_dbg[c_offset(row0, row, 2 * I, hbase + col, 0)] = gv;
+              prm.c1_dbg[c_offset(row0, row, 2 * I, I + hbase + col, 0)] = uv;
             }
-            if (prm.h_dbg) prm.h_dbg[p * I + hbase + col] = (uint16_t)hb;
+            if (prm.h_dbg) prm.h_dbg[c_offset(row0, row, I, hbase + col, 0)] = (uint16_t)hb;
           }
         }
     }
@@ -713,14 +660,13 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
         const int row = item / kPieces, pc = item % kPieces;
         const int32_t hcol = hbase + 8 * pc;
         if (row < rows && hcol < I)
-          *reinterpret_cast<u32x4*>(prm.h_out + (int64_t)(row0 + row) * I + hcol) =
+          *reinterpret_cast<u32x4*>(prm.h_out + a_rows_offset(row0 + row, I, hcol / 8, 8)) =
               *reinterpret_cast<const u32x4*>(sh + row * kLdh + 8 * pc);
       }
     } else if constexpr (kMX) {
       // requantise in the UE8M0 mode: rows x (kHW / 32) blocks of 32 columns
       constexpr int kItems = 32 * kMBa * (kHW / 32);
       const float gs = prm.out_gscale[e];
-      const int64_t ob2 = I / 2, ob32 = I / 32;
       for (int item = tid; item < kItems; item += kThreads) {
         const int row = item / (kHW / 32), blk = item % (kHW / 32);
         const int32_t hcol = hbase + 32 * blk;
@@ -737,15 +683,14 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
           wv.z = encode8(xv + 16, bsc.inv);
           wv.w = encode8(xv + 24, bsc.inv);
           const int64_t p = row0 + row;
-          *reinterpret_cast<u32x4*>(prm.out_codes + p * ob2 + hcol / 2) = wv;
-          prm.out_sf[p * ob32 + hcol / 32] = (uint8_t)bsc.sf;
+          *reinterpret_cast<u32x4*>(prm.out_codes + a_codes_offset(p, I, hcol / 32, 32, true)) = wv;
+          prm.out_sf[a_scales_offset(p, I, hcol / 32, 32, true)] = (uint8_t)bsc.sf;
         }
       }
     } else {
     // requantise: rows x (kHW / 16) blocks of 16 columns
     constexpr int kItems = 32 * kMBa * (kHW / 16);
     const float gs = prm.out_gscale[e];
-    const int64_t ob2 = I / 2, ob16 = I / 16;
     for (int item = tid; item < kItems; item += kThreads) {
       const int row = item / (kHW / 16), blk = item % (kHW / 16);
       const int32_t hcol = hbase + 16 * blk;
@@ -759,8 +704,8 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
         wv.x = encode8(xv, bsc.inv);
         wv.y = encode8(xv + 8, bsc.inv);
         const int64_t p = row0 + row;
-        *reinterpret_cast<uint2*>(prm.out_codes + p * ob2 + hcol / 2) = wv;
-        prm.out_sf[p * ob16 + hcol / 16] = (uint8_t)bsc.sf;
+        *reinterpret_cast<uint2*>(prm.out_codes + a_codes_offset(p, I, hcol / 16, 16, false)) = wv;
+        prm.out_sf[a_scales_offset(p, I, hcol / 16, 16, false)] = (uint8_t)bsc.sf;
       }
     }
     }
@@ -788,10 +733,6 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
 }
 
 namespace {
-
-int32_t m_tiles_bound(int32_t P, int32_t E, int32_t bm) {
-  return (P + bm - 1) / bm + (P < E ? P : E);
-}
 
 // Resident workgroups per CU for a kernel, and the CU count, for the current
 // device (every device this library runs on is the same gfx950 part).
@@ -839,9 +780,16 @@ hipError_t launch(GemmParams prm, int32_t P, hipStream_t stream) {
 
 }  // namespace
 
-// Tile height: 128 token rows when experts average at least 32 rows (prefill;
-// the last tile of an expert runs only its occupied 32-row sub-tiles), else
-// 32 (decode-like batches, weight-streaming bound).
+// The kernel instantiation for a gemm_map::Shape and operand mode.
+template <int kMode, const Shape& S>
+hipError_t launch_shape(const GemmParams& prm, int32_t P, hipStream_t stream) {
+  return launch<S.waves, S.mb, S.bk, S.gated, S.ring, S.occ, kMode>(prm, P, stream);
+}
+
+// Shapes by batch (gemm_map::select_shape): the large-batch tiles when experts
+// average at least 32 rows (prefill; the last tile of an expert runs only its
+// occupied 32-row sub-tiles), else 32-row tiles (decode-like batches, weight
+// streaming bound).
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream) {
   if (a.P == 0) return hipSuccess;
   GemmParams prm{};
@@ -853,24 +801,15 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream) {
   prm.out_gscale = a.out_gscale; prm.out_codes = a.out_codes; prm.out_sf = a.out_sf;
   prm.c1_dbg = a.c1_dbg; prm.h_dbg = a.h_dbg;
   const int mode = a.mx ? kModeMX : a.w16 ? kModeW16 : kModeNV;
-  if (a.P >= 32 * a.E) {
-    prm.n_tiles = (a.I + 32 * kG1Waves - 1) / (32 * kG1Waves);
-#define NVFP4_G1(m) return launch<kG1Waves, kG1MB, kG1BK, true, kG1Ring, kG1Occ, m>(prm, a.P, stream)
-    if (mode == kModeMX)
-      return launch<kG1Waves, kG1MBmx, kG1BKmx, true, kG1RingMx, kG1Occ, kModeMX>(prm, a.P, stream);
-    if (mode == kModeW16)
-      return launch<kG1Waves, kG1MBw16, kG1BK, true, kG1RingW16, kG1Occ, kModeW16>(prm, a.P, stream);
-    NVFP4_G1(kModeNV);
-#undef NVFP4_G1
+  prm.n_tiles = n_tiles(true, select_shape(true, mode, a.P, a.E).waves, a.I, a.H);
+  if (large_batch(a.P, a.E)) {
+    if (mode == kModeMX) return launch_shape<kModeMX, kG1LargeMx>(prm, a.P, stream);
+    if (mode == kModeW16) return launch_shape<kModeW16, kG1LargeW16>(prm, a.P, stream);
+    return launch_shape<kModeNV, kG1Large>(prm, a.P, stream);
   }
-  constexpr int kWaves = 4;
-  prm.n_tiles = (a.I + 32 * kWaves - 1) / (32 * kWaves);
-#define NVFP4_G1(m) return launch<kWaves, 1, kG1BK, true, kS1Ring, 2, m>(prm, a.P, stream)
-  if (mode == kModeMX)
-    return launch<kWaves, 1, kG1BKmx, true, kS1Ring, 2, kModeMX>(prm, a.P, stream);
-  if (mode == kModeW16) NVFP4_G1(kModeW16);
-  NVFP4_G1(kModeNV);
-#undef NVFP4_G1
+  if (mode == kModeMX) return launch_shape<kModeMX, kG1SmallMx>(prm, a.P, stream);
+  if (mode == kModeW16) return launch_shape<kModeW16, kG1Small>(prm, a.P, stream);
+  return launch_shape<kModeNV, kG1Small>(prm, a.P, stream);
 }
 
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream) {
@@ -881,22 +820,16 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream) {
   prm.in_scale = a.in_scale; prm.w_scale2 = a.w_scale2; prm.offsets = a.offsets;
   prm.E = a.E; prm.K = a.I; prm.N_w = a.H; prm.I = a.I;
   prm.c_out = a.out; prm.ldc = a.H;
-  constexpr int kWaves = 4;
-  prm.n_tiles = (a.H + 64 * kWaves - 1) / (64 * kWaves);
   const int mode = a.mx ? kModeMX : a.w16 ? kModeW16 : kModeNV;
-  if (a.P >= 32 * a.E) {
-#define NVFP4_G2(m) return launch<kWaves, kG2MB, 64, false, kG2Ring, kG2Occ, m>(prm, a.P, stream)
-    if (mode == kModeMX)
-      return launch<kWaves, kG2MB, 64, false, kG2RingMx, kG2Occ, kModeMX>(prm, a.P, stream);
-    if (mode == kModeW16) NVFP4_G2(kModeW16);
-    NVFP4_G2(kModeNV);
-#undef NVFP4_G2
+  prm.n_tiles = n_tiles(false, select_shape(false, mode, a.P, a.E).waves, a.I, a.H);
+  if (large_batch(a.P, a.E)) {
+    if (mode == kModeMX) return launch_shape<kModeMX, kG2LargeMx>(prm, a.P, stream);
+    if (mode == kModeW16) return launch_shape<kModeW16, kG2Large>(prm, a.P, stream);
+    return launch_shape<kModeNV, kG2Large>(prm, a.P, stream);
   }
-#define NVFP4_G2(m) return launch<kWaves, 1, 64, false, kS2Ring, 2, m>(prm, a.P, stream)
-  if (mode == kModeMX) NVFP4_G2(kModeMX);
-  if (mode == kModeW16) NVFP4_G2(kModeW16);
-  NVFP4_G2(kModeNV);
-#undef NVFP4_G2
+  if (mode == kModeMX) return launch_shape<kModeMX, kG2Small>(prm, a.P, stream);
+  if (mode == kModeW16) return launch_shape<kModeW16, kG2Small>(prm, a.P, stream);
+  return launch_shape<kModeNV, kG2Small>(prm, a.P, stream);
 }
 
 // ---- load-time weight layout conversion -----------------------------------
@@ -947,7 +880,12 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restr
 }
 
 int32_t weight_step_k(int32_t projection, bool mx) {
-  return projection == 0 ? (mx ? kG1BKmx : kG1BK) : 64;
+  // every GEMM1 shape of a mode shares one K step, as every GEMM2 shape does
+  static_assert(kG1Large.bk == kG1Small.bk && kG1Large.bk == kG1LargeW16.bk &&
+                kG1LargeMx.bk == kG1SmallMx.bk, "one w13 K step per mode");
+  static_assert(kG2Large.bk == kG2Small.bk && kG2Large.bk == kG2LargeMx.bk,
+                "one w2 K step");
+  return projection == 0 ? (mx ? kG1LargeMx.bk : kG1Large.bk) : kG2Large.bk;
 }
 
 hipError_t launch_pack_weights(int32_t projection, const uint8_t* codes, const uint8_t* sf,
