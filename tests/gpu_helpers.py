@@ -77,15 +77,24 @@ def dot_error_bound(a_norm, w_norm, alpha, row_expert, K):
     return scale[:, None] * w_norm[e]
 
 
-def weight_row_norms(layer, proj: str, dequant):
-    """||dequantised W[e][n]|| for every expert e and weight row n (cached on
-    the layer)."""
+def weight_row_norms(layer, proj: str, dequant, experts=None):
+    """||dequantised W[e][n]|| for every weight row n of the given experts
+    (all by default), as an [E, N] array; rows of experts not asked for are
+    NaN, so a bound built from them rejects everything.  Cached on the layer
+    per expert."""
+    codes, sf = (layer.w13c, layer.w13s) if proj == "w13" else (layer.w2c, layer.w2s)
     key = f"_norms_{proj}"
     if not hasattr(layer, key):
-        codes, sf = (layer.w13c, layer.w13s) if proj == "w13" else (layer.w2c, layer.w2s)
-        setattr(layer, key, np.stack([np.linalg.norm(dequant(codes[e], sf[e]), axis=1)
-                                      for e in range(codes.shape[0])]))
-    return getattr(layer, key)
+        setattr(layer, key, {})
+    cache = getattr(layer, key)
+    want = range(codes.shape[0]) if experts is None else [int(e) for e in experts]
+    for e in want:
+        if e not in cache:
+            cache[e] = np.linalg.norm(dequant(codes[e], sf[e]), axis=1)
+    out = np.full((codes.shape[0], codes.shape[1]), np.nan)
+    for e, v in cache.items():
+        out[e] = v
+    return out
 
 
 def routing_weight_bound(logits, ids, w_ref):
@@ -347,3 +356,83 @@ def check_layer_parity_w4a16(layer: OM.Layer, x_bits, logits, k, residual_bits=N
     return dict(c1_max=float(c1.max()), h_max=float(hr.max()), c2_max=float(c2.max()),
                 out_max=float(outr.max()), out_median=float(np.median(outr)),
                 e2e_max=float(e2e.max()), h_diffs_vs_own=h_diffs, got=got, ref=ref)
+
+
+def gather_token_subset(dev, logits, k, E, tokens, label=""):
+    """From one full-batch GPU forward's device tensors ``dev`` (the debug
+    dumps and "out"): check the routing ids and the permutation of the whole
+    batch exactly against the oracle's router and permutation, and the
+    routing weights within the fp32 softmax bound; then gather, as host
+    arrays, the rows that a subset of tokens produced, in the order of the
+    subset's own permutation (which the oracle's layer on the subset alone
+    forms).  Returns the gathered arrays for check_gathered_subset."""
+    import torch
+    tokens = np.asarray(tokens, dtype=np.int64)
+    assert np.array_equal(tokens, np.unique(tokens)), "sorted distinct tokens"
+    ids, w = OM.route(logits, k)
+    assert np.array_equal(dev["topk_ids"].cpu().numpy(), ids), label + " routing ids"
+    w_err = routing_weight_bound(logits, ids, w)
+    assert np.all(np.abs(dev["topk_weights"].cpu().numpy() - w) <= w_err), (
+        label, "routing weights")
+    offsets, src_pair, inv = OM.permute(ids, E)
+    assert np.array_equal(dev["expert_offsets"].cpu().numpy(), offsets), label + " offsets"
+    assert np.array_equal(dev["src_pair"].cpu().numpy(), src_pair), label + " src_pair"
+    assert np.array_equal(dev["inv_pair"].cpu().numpy(), inv), label + " inv_pair"
+    sub_ids, _ = OM.route(np.asarray(logits)[tokens], k)
+    _, sub_src, _ = OM.permute(sub_ids, E)
+    qs = sub_src.astype(np.int64)
+    rows = inv[tokens[qs // k] * k + qs % k].astype(np.int64)
+    rows_d = torch.from_numpy(rows).to(dev["c1"].device)
+    got = {name: dev[name].index_select(0, rows_d).cpu().numpy()
+           for name in ("a1_codes", "a1_sf", "c1", "h", "a2_codes", "a2_sf", "c2")}
+    got["h"] = got["h"].view(np.uint16)
+    tok_d = torch.from_numpy(tokens).to(dev["c1"].device)
+    got["out"] = dev["out"].view(torch.int16).index_select(0, tok_d).cpu().numpy().view(
+        np.uint16)
+    return got
+
+
+def check_gathered_subset(layer: OM.Layer, x_sub, logits_sub, k, res_sub, got, label=""):
+    """Stage-by-stage parity of the gathered rows of a subset of tokens
+    (gather_token_subset) against the oracle's layer on those tokens alone;
+    the MoE layer treats tokens independently, so that is the reference for
+    those rows of the full batch.  A1 codes and scales exactly; C1 per row
+    within REL_L2_TOL and element-wise within the fp32 accumulation bound; h
+    correctly rounded; A2 the oracle quantiser's image of the GPU's h; C2 over
+    the GPU's A2 as C1; the output correctly rounded from that C2's combine.
+    CPU only.  Returns per-stage maxima."""
+    E, I, H = layer.E, layer.I, layer.H
+    nt = x_sub.shape[0]
+    ref = OM.layer_forward(layer, x_sub, logits_sub, k, res_sub)
+    assert np.array_equal(got["a1_codes"], ref["a1"][0]), label + " A1 codes"
+    assert np.array_equal(got["a1_sf"], ref["a1"][1]), label + " A1 scales"
+    rexp = OM.row_experts(ref["offsets"])
+    hit = np.unique(rexp)
+    c1 = rel_l2_rows(got["c1"], ref["c1"])
+    assert c1.max() <= REL_L2_TOL, (label, "C1", c1.max())
+    err_c1 = dot_error_bound(np.linalg.norm(OQ.dequant(*ref["a1"]), axis=1),
+                             weight_row_norms(layer, "w13", OQ.dequant, hit), layer.alpha1,
+                             rexp, H)
+    assert np.all(np.abs(got["c1"] - ref["c1"]) <= err_c1), (label, "C1 elements")
+    h_exact = OM.silu_mul(ref["c1"], I)
+    assert_correctly_rounded_bf16(bf16_f64(got["h"]), h_exact,
+                                  silu_mul_error_bound(ref["c1"], err_c1, I), label + " h")
+    a2c, a2s = OQ.quantize_experts(got["h"], rexp, ref["a2_gscale"])
+    assert np.array_equal(got["a2_codes"], a2c), label + " A2 codes vs Q(h_gpu)"
+    assert np.array_equal(got["a2_sf"], a2s), label + " A2 scales vs Q(h_gpu)"
+    c2_ref = OM.grouped_gemm_ref(got["a2_codes"], got["a2_sf"], ref["offsets"], layer.w2c,
+                                 layer.w2s, layer.alpha2)
+    c2 = rel_l2_rows(got["c2"], c2_ref)
+    assert c2.max() <= REL_L2_TOL, (label, "C2", c2.max())
+    err_c2 = dot_error_bound(np.linalg.norm(OQ.dequant(got["a2_codes"], got["a2_sf"]), axis=1),
+                             weight_row_norms(layer, "w2", OQ.dequant, hit), layer.alpha2,
+                             rexp, I)
+    assert np.all(np.abs(got["c2"] - c2_ref) <= err_c2), (label, "C2 elements")
+    res_f = None if res_sub is None else OF.bf16_to_f32(res_sub)
+    out_ref = OM.combine_ref(c2_ref, ref["w"], ref["inv"], nt, k, res_f)
+    w_err = routing_weight_bound(logits_sub, ref["ids"], ref["w"])
+    err_out = combine_error_bound(c2_ref, err_c2, ref["w"], w_err, ref["inv"], nt, k, res_f)
+    out_gpu = bf16_f64(got["out"])
+    assert_correctly_rounded_bf16(out_gpu, out_ref, err_out, label + " out")
+    return dict(c1_max=float(c1.max()), c2_max=float(c2.max()),
+                out_max=float(rel_l2_rows(out_gpu, out_ref).max()), experts_hit=int(hit.size))

@@ -99,10 +99,12 @@ def test_prefill_layer():
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("layer_idx", [0, 29])
+@pytest.mark.parametrize("layer_idx", [0])
 def test_stack_layer(layer_idx):
     """One layer of the 30-layer stack (its own weights, scales and Zipf
-    router) on a seeded N(0,1) input and residual of the stack's shape."""
+    router) on a seeded N(0,1) input and residual of the stack's shape, every
+    row checked (the whole chain, on a subset of rows per layer, is in
+    test_gpu_stack.py)."""
     w = S.WORKLOADS["stack"]
     layer = oracle_layer("stack", layer_idx)
     x = S.activations(w, layer=layer_idx)

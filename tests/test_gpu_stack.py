@@ -1,0 +1,145 @@
+"""The 30-layer stack as a chain on the GPU: 8192 tokens, hidden 2816, 128
+experts, intermediate 704, top-8 with Zipf(1.1)-skewed routing that leaves
+experts without tokens; x_{l+1} = bf16(x_l + MoE_l(x_l)), each layer with its
+own weights, scales and router (the 30-layer stack of the model the pages
+describe; their missing-scale failure corrupts later layers through this
+residual path).
+
+Every layer is checked against the oracle teacher-forced on that layer's GPU
+input: routing ids and the permutation over the whole batch exactly; on a
+seeded subset of 32 tokens the A1 codes and scales exactly, C1 and C2 per row
+within 2e-3 relative L2 and element-wise within the fp32 bound, h and A2
+against the oracle, and the output element by element.  The MoE layer treats
+tokens independently, so the oracle's layer on the subset's rows is the
+reference for those rows of the full batch.  The drift of the GPU chain from
+the oracle's own chain (no teacher forcing) on 4 of those tokens is
+reported, not asserted.
+
+The oracle's work (preparing each layer, and checking each layer's gathered
+rows) runs in worker processes beside the chain (tests/stack_oracle.py); a
+layer's verdict may arrive while a later layer runs, and the last test waits
+for every verdict."""
+import multiprocessing
+import time
+from concurrent.futures import ProcessPoolExecutor
+
+import numpy as np
+import pytest
+
+import synthetic as S
+from oracle import formats as OF
+from oracle import moe as OM
+
+from gpu_helpers import device_layer, gather_token_subset, progress, rel_l2_rows
+import stack_oracle
+
+pytestmark = pytest.mark.gpu
+
+W = S.WORKLOADS["stack"]
+N_CHECK = 32          # tokens checked stage by stage in every layer
+N_OWN = 4             # tokens followed through the oracle's own chain
+WORKERS = 6           # oracle worker processes (3 threads each)
+AHEAD = 4             # layers prepared ahead of the chain
+_chain = {}
+
+
+def _pool():
+    if "pool" not in _chain:
+        ctx = multiprocessing.get_context("spawn")
+        _chain["pool"] = ProcessPoolExecutor(max_workers=WORKERS, mp_context=ctx)
+        _chain["prep"] = {}
+        _chain["checks"] = {}
+        _chain["verdicts"] = {}
+    return _chain["pool"]
+
+
+def _request(l):
+    if l < W.layers and l not in _chain["prep"]:
+        _chain["prep"][l] = _pool().submit(stack_oracle.prepare_stack_layer, l)
+
+
+def _collect(wait=False):
+    """Record the verdicts of finished layer checks (all of them if wait);
+    raise for the first layer whose check failed."""
+    for l in sorted(_chain["checks"]):
+        fut = _chain["checks"][l]
+        if not (wait or fut.done()):
+            continue
+        del _chain["checks"][l]
+        m = fut.result()                     # re-raises the check's AssertionError
+        _chain["verdicts"][l] = m
+        print(f"[stack L{l}] verdict: subset rel-L2 per row C1 max {m['c1_max']:.2e}  C2 max "
+              f"{m['c2_max']:.2e}  out max {m['out_max']:.2e} ({m['experts_hit']} experts; "
+              f"oracle check {m['check_seconds']:.1f} s)", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _shutdown_pool():
+    yield
+    pool = _chain.pop("pool", None)
+    if pool is not None:
+        pool.shutdown(wait=True, cancel_futures=True)
+    _chain.clear()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("l", range(W.layers))
+def test_stack_chain_layer(l):
+    import torch
+    from nvfp4_w4a4_expert_amd import moe as M
+    if l == 0:
+        _pool()
+        x0 = S.activations(W, layer=0)
+        rng = np.random.default_rng(2026)
+        tokens = np.sort(rng.choice(W.T, N_CHECK, replace=False))
+        _chain.update(x=M.bf16_tensor(x0), tokens=tokens, own=x0[tokens[:N_OWN]], drift=[])
+    assert "x" in _chain, "the chain's earlier layers did not run"
+    for j in range(l, l + AHEAD + 1):
+        _request(j)
+    t0 = time.perf_counter()
+    fields = _chain["prep"].pop(l).result()
+    t1 = time.perf_counter()
+    layer = stack_oracle.layer_from_fields(fields)
+    prep_s = fields.pop("prep_seconds")
+    tokens = _chain["tokens"]
+    x = _chain.pop("x")
+    logits = S.router_logits(W, layer=l)
+    dl = device_layer(layer)
+    out, dev = dl.forward(x, torch.from_numpy(logits).cuda(), W.k, residual=x, debug=True)
+    dev["out"] = out
+    torch.cuda.synchronize()
+    del dl
+    counts = np.diff(dev["expert_offsets"].cpu().numpy())
+    assert np.count_nonzero(counts == 0) >= 1            # Zipf routing leaves experts empty
+    x_sub = M.bf16_bits(x.index_select(0, torch.from_numpy(tokens).cuda()))
+    got = gather_token_subset(dev, logits, W.k, W.E, tokens, label=f"stack L{l}")
+    del dev, x
+    t2 = time.perf_counter()
+    _chain["checks"][l] = _pool().submit(stack_oracle.check_stack_layer, fields, x_sub,
+                                         logits[tokens], W.k, got, f"stack L{l}")
+    t3 = time.perf_counter()
+    # the oracle's own chain on a few tokens (informational drift)
+    own = OM.layer_forward(layer, _chain["own"], logits[tokens[:N_OWN]], W.k,
+                           _chain["own"])["out_bf16"]
+    _chain["own"] = own
+    drift = rel_l2_rows(OF.bf16_to_f32(got["out"][:N_OWN]), OF.bf16_to_f32(own)).max()
+    _chain["drift"].append(float(drift))
+    _chain["x"] = out
+    t4 = time.perf_counter()
+    print(f"[stack L{l}] GPU layer done: {int(np.count_nonzero(counts == 0))} experts without "
+          f"rows; drift of the GPU chain from the oracle's own chain {drift:.2e} (waited "
+          f"{t1 - t0:.1f} s for the oracle's layer, prepared in {prep_s:.1f} s; GPU and gather "
+          f"{t2 - t1:.1f} s, check "
+          f"hand-off {t3 - t2:.1f} s, own chain {t4 - t3:.1f} s)", flush=True)
+    _collect()
+
+
+@pytest.mark.timeout(600)
+def test_stack_chain_every_layer_checked():
+    assert "pool" in _chain, "the chain did not run"
+    progress("stack: waiting for the remaining layer checks")
+    _collect(wait=True)
+    assert sorted(_chain["verdicts"]) == list(range(W.layers))
+    print(f"[stack] all {W.layers} layers match the oracle teacher-forced; drift of the GPU "
+          f"chain from the oracle's own chain after {W.layers} layers: "
+          f"{_chain['drift'][-1]:.2e} (max rel-L2 per row over {N_OWN} tokens)", flush=True)
