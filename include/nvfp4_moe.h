@@ -75,7 +75,7 @@ NVFP4_API const char* nvfp4_status_string(nvfp4_status_t status);
 
 /* ABI revision of this header; bumped on any incompatible change. */
 NVFP4_API int32_t nvfp4_abi_version(void);
-#define NVFP4_ABI_VERSION 5
+#define NVFP4_ABI_VERSION 6
 
 /*
  * nvfp4_validate_scales — the load-time completeness check (page 3, "ROOT
@@ -106,19 +106,64 @@ NVFP4_API nvfp4_status_t nvfp4_validate_scales(const float* input_scale, const u
 /*
  * nvfp4_quantize_experts — dynamic per-expert NVFP4 activation quantisation
  * (page 3, "NVFP4" section: runtime-order figure and the
- * SFScale[expert_idx] excerpt).  For every (row t, slot j) pair
- * q = t*topk + j, with e = expert_idx[q] (0 when expert_idx is NULL) and
- * SFScaleVal = gscale ? gscale[e] : 1.0f, row t of x is quantised in blocks
- * of 16 along K and written to destination row p = dst_row ? dst_row[q] : q:
+ * SFScale[expert_idx] excerpt), over rows already grouped by expert.  Row p
+ * of the output belongs to the expert e with expert_offsets[e] <= p <
+ * expert_offsets[e+1] and quantises source row s = src_row ? src_row[p] : p
+ * of x in blocks of 16 along K, with SFScaleVal = gscale ? gscale[e] : 1.0f:
  *     amax = max|x|;  s = fl32(SFScaleVal * fl32(amax / 6));
  *     sf = E4M3(s) (nearest, ties to even, saturating at 448);
  *     v = fl32(x * min(fl32(SFScaleVal / E4M3value(sf)), FLT_MAX)), or 0 when
  *     the E4M3 value is 0;  code = E2M1(v) (nearest, ties to even,
  *     saturating at 6, sign kept).
- * Each source row is read once for all of its topk destinations.
+ *
+ *   x_bf16          device bf16 [num_src_rows, ldx]; 16-byte aligned, ldx % 8 == 0.
+ *   ldx             row stride of x in elements (>= K).
+ *   K               elements per row; K % 16 == 0.
+ *   src_row         device int32 [P] or NULL (identity: row p reads row p,
+ *                   and then num_src_rows >= P is required).
+ *   num_src_rows    rows of x; output rows whose source row falls outside
+ *                   [0, num_src_rows) are not written.
+ *   P               output rows; 0 is a no-op.
+ *   expert_offsets  device int32 [E+1], non-decreasing; output rows outside
+ *                   [expert_offsets[0], expert_offsets[E]) are not written.
+ *   E               experts (length of gscale), >= 1.
+ *   gscale          device fp32 [E] or NULL (=> 1.0f, the page's null-SFScale
+ *                   case).  Values must come from nvfp4_validate_scales.
+ *   codes           device uint8 [P, K/2], 8-byte aligned.
+ *   sf              device uint8 [P, K/16].
+ * NVFP4_ERR_INVALID_ARG for a bad size, a NULL required pointer or a
+ * misaligned x / codes, before anything is enqueued.
+ */
+NVFP4_API nvfp4_status_t nvfp4_quantize_experts(const void* x_bf16, int64_t ldx, int32_t K,
+                                                const int32_t* src_row, int32_t num_src_rows,
+                                                int32_t P, const int32_t* expert_offsets,
+                                                int32_t E, const float* gscale, uint8_t* codes,
+                                                uint8_t* sf, nvfp4_stream_t stream);
+
+/*
+ * nvfp4_quantize_experts_fp16 — the same quantiser for fp16 source rows
+ * (page 3, "NVFP4" runtime-order figure: the hidden state entering the
+ * quantiser is BF16 or FP16).  Every fp16 value converts exactly to fp32, so
+ * the arithmetic above applies unchanged.  Arguments, layouts, ownership and
+ * errors as for nvfp4_quantize_experts, with x_fp16 device fp16
+ * [num_src_rows, ldx], 16-byte aligned, ldx % 8 == 0.
+ */
+NVFP4_API nvfp4_status_t nvfp4_quantize_experts_fp16(const void* x_fp16, int64_t ldx, int32_t K,
+                                                     const int32_t* src_row, int32_t num_src_rows,
+                                                     int32_t P, const int32_t* expert_offsets,
+                                                     int32_t E, const float* gscale,
+                                                     uint8_t* codes, uint8_t* sf,
+                                                     nvfp4_stream_t stream);
+
+/*
+ * nvfp4_quantize_pairs — the same quantisation, fused with the regrouping by
+ * expert: the form the layer forward runs, which reads each token row once
+ * for all of its topk destinations.  For every (row t, slot j) pair
+ * q = t*topk + j, with e = expert_idx[q] (0 when expert_idx is NULL), row t of
+ * x is quantised with SFScaleVal = gscale ? gscale[e] : 1.0f and written to
+ * output row p = dst_row ? dst_row[q] : q.
  *
  *   x_bf16        device bf16 [num_rows, ldx]; 16-byte aligned, ldx % 8 == 0.
- *   ldx           row stride of x in elements (>= K).
  *   num_rows      rows of x (tokens); 0 is a no-op.
  *   K             elements per row; K % 16 == 0.
  *   topk          destinations per source row (>= 1).
@@ -128,33 +173,15 @@ NVFP4_API nvfp4_status_t nvfp4_validate_scales(const float* input_scale, const u
  *                 falls outside [0, num_dst_rows) / [0, num_experts) are
  *                 skipped.
  *   num_experts   length of gscale (>= 1).
- *   gscale        device fp32 [num_experts] or NULL (=> 1.0f, the page's
- *                 null-SFScale case).  Values must come from
- *                 nvfp4_validate_scales.
+ *   gscale        device fp32 [num_experts] or NULL (=> 1.0f).
  *   codes         device uint8 [num_dst_rows, K/2], 8-byte aligned.
  *   sf            device uint8 [num_dst_rows, K/16].
  */
-NVFP4_API nvfp4_status_t nvfp4_quantize_experts(const void* x_bf16, int64_t ldx, int32_t num_rows,
-                                                int32_t K, int32_t topk, const int32_t* expert_idx,
-                                                const int32_t* dst_row, int32_t num_experts,
-                                                const float* gscale, uint8_t* codes, uint8_t* sf,
-                                                int32_t num_dst_rows, nvfp4_stream_t stream);
-
-/*
- * nvfp4_quantize_experts_fp16 — the same quantiser for fp16 source rows
- * (page 3, "NVFP4" runtime-order figure: the hidden state entering the
- * quantiser is BF16 or FP16).  Every fp16 value converts exactly to fp32, so
- * the arithmetic above applies unchanged.  Arguments, layouts, ownership and
- * errors as for nvfp4_quantize_experts, with x_fp16 device fp16
- * [num_rows, ldx], 16-byte aligned, ldx % 8 == 0.
- */
-NVFP4_API nvfp4_status_t nvfp4_quantize_experts_fp16(const void* x_fp16, int64_t ldx,
-                                                     int32_t num_rows, int32_t K, int32_t topk,
-                                                     const int32_t* expert_idx,
-                                                     const int32_t* dst_row, int32_t num_experts,
-                                                     const float* gscale, uint8_t* codes,
-                                                     uint8_t* sf, int32_t num_dst_rows,
-                                                     nvfp4_stream_t stream);
+NVFP4_API nvfp4_status_t nvfp4_quantize_pairs(const void* x_bf16, int64_t ldx, int32_t num_rows,
+                                              int32_t K, int32_t topk, const int32_t* expert_idx,
+                                              const int32_t* dst_row, int32_t num_experts,
+                                              const float* gscale, uint8_t* codes, uint8_t* sf,
+                                              int32_t num_dst_rows, nvfp4_stream_t stream);
 
 /*
  * nvfp4_route_topk — the router's choice of expert_idx (page 3, "NVFP4"
@@ -251,7 +278,7 @@ NVFP4_API nvfp4_status_t nvfp4_calibrate_input_scales(const void* x_bf16, int64_
  *       FP8 conversion) vs nearest-even saturating rounding, every
  *       non-negative fp32 input and +inf;
  *   [4] E4M3 -> fp32 vs the OCP E4M3 definition, all 127 non-negative codes.
- * All three must read 0.
+ * All five must read 0.
  */
 NVFP4_API nvfp4_status_t nvfp4_selftest_conversions(unsigned long long* mismatches,
                                                     nvfp4_stream_t stream);
@@ -430,17 +457,23 @@ NVFP4_API nvfp4_status_t nvfp4_moe_forward_w4a16(const nvfp4_moe_weights_t* w,
  */
 
 /*
- * nvfp4_quantize_experts_mx — nvfp4_quantize_experts in the UE8M0 mode.  Same
- * arguments and behaviour, except: K % 32 == 0, and sf is [num_dst_rows, K/32]
- * UE8M0 codes (one per 32 elements).
+ * nvfp4_quantize_experts_mx / nvfp4_quantize_pairs_mx — nvfp4_quantize_experts
+ * and nvfp4_quantize_pairs in the UE8M0 mode.  Same arguments and
+ * behaviour, except: K % 32 == 0, and sf is [rows, K/32] UE8M0 codes (one per
+ * 32 elements).
  */
-NVFP4_API nvfp4_status_t nvfp4_quantize_experts_mx(const void* x_bf16, int64_t ldx,
-                                                   int32_t num_rows, int32_t K, int32_t topk,
-                                                   const int32_t* expert_idx,
-                                                   const int32_t* dst_row, int32_t num_experts,
-                                                   const float* gscale, uint8_t* codes,
-                                                   uint8_t* sf, int32_t num_dst_rows,
-                                                   nvfp4_stream_t stream);
+NVFP4_API nvfp4_status_t nvfp4_quantize_experts_mx(const void* x_bf16, int64_t ldx, int32_t K,
+                                                   const int32_t* src_row, int32_t num_src_rows,
+                                                   int32_t P, const int32_t* expert_offsets,
+                                                   int32_t E, const float* gscale, uint8_t* codes,
+                                                   uint8_t* sf, nvfp4_stream_t stream);
+NVFP4_API nvfp4_status_t nvfp4_quantize_pairs_mx(const void* x_bf16, int64_t ldx,
+                                                 int32_t num_rows, int32_t K, int32_t topk,
+                                                 const int32_t* expert_idx,
+                                                 const int32_t* dst_row, int32_t num_experts,
+                                                 const float* gscale, uint8_t* codes,
+                                                 uint8_t* sf, int32_t num_dst_rows,
+                                                 nvfp4_stream_t stream);
 
 /*
  * nvfp4_moe_pack_weights_mx — nvfp4_moe_pack_weights for UE8M0 weights:

@@ -59,8 +59,9 @@ _SIGS = {
     "nvfp4_status_string": (ctypes.c_char_p, [_i32]),
     "nvfp4_abi_version": (_i32, []),
     "nvfp4_validate_scales": (_i32, [_p, _p, _i32, _p, _p, _p]),
-    "nvfp4_quantize_experts": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _p, _i32, _p, _p, _p, _i32, _p]),
-    "nvfp4_quantize_experts_fp16": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _p, _i32, _p, _p, _p, _i32, _p]),
+    "nvfp4_quantize_experts": (_i32, [_p, _i64, _i32, _p, _i32, _i32, _p, _i32, _p, _p, _p, _p]),
+    "nvfp4_quantize_pairs": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _p, _i32, _p, _p, _p, _i32, _p]),
+    "nvfp4_quantize_experts_fp16": (_i32, [_p, _i64, _i32, _p, _i32, _i32, _p, _i32, _p, _p, _p, _p]),
     "nvfp4_route_topk": (_i32, [_p, _i32, _i32, _i32, _p, _p, _p]),
     "nvfp4_permute": (_i32, [_p, _i32, _i32, _i32, _p, _p, _p, _p]),
     "nvfp4_expert_absmax": (_i32, [_p, _i64, _i32, _p, _i32, _p, _i32, _i32, _p, _p]),
@@ -70,7 +71,8 @@ _SIGS = {
     "nvfp4_moe_workspace_size": (_i32, [_i32, _i32, ctypes.POINTER(MoEWeights), ctypes.POINTER(ctypes.c_size_t)]),
     "nvfp4_moe_forward": (_i32, [ctypes.POINTER(MoEWeights), _p, _p, _i32, _i32, _p, _p, _p,
                                  ctypes.c_size_t, ctypes.POINTER(MoEDebug), _p]),
-    "nvfp4_quantize_experts_mx": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _p, _i32, _p, _p, _p, _i32, _p]),
+    "nvfp4_quantize_experts_mx": (_i32, [_p, _i64, _i32, _p, _i32, _i32, _p, _i32, _p, _p, _p, _p]),
+    "nvfp4_quantize_pairs_mx": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _p, _i32, _p, _p, _p, _i32, _p]),
     "nvfp4_moe_pack_weights_mx": (_i32, [_i32, _p, _p, _i32, _i32, _i32, _p, _p, _p]),
     "nvfp4_moe_forward_mx": (_i32, [ctypes.POINTER(MoEWeights), _p, _p, _i32, _i32, _p, _p, _p,
                                     ctypes.c_size_t, ctypes.POINTER(MoEDebug), _p]),
@@ -138,20 +140,28 @@ def validate_scales(input_scale: np.ndarray, written: Optional[np.ndarray] = Non
 
 # --- device -----------------------------------------------------------------
 
-def quantize_experts(x, ldx: int, num_rows: int, K: int, topk: int, expert_idx, dst_row,
-                     num_experts: int, gscale, codes, sf, num_dst_rows: int, stream=None):
-    _check(_lib.nvfp4_quantize_experts(_ptr(x), ldx, num_rows, K, topk, _ptr(expert_idx),
-                                       _ptr(dst_row), num_experts, _ptr(gscale), _ptr(codes),
-                                       _ptr(sf), num_dst_rows, _stream(stream)),
+def quantize_experts(x, ldx: int, K: int, src_row, num_src_rows: int, P: int, expert_offsets,
+                     num_experts: int, gscale, codes, sf, stream=None):
+    _check(_lib.nvfp4_quantize_experts(_ptr(x), ldx, K, _ptr(src_row), num_src_rows, P,
+                                       _ptr(expert_offsets), num_experts, _ptr(gscale),
+                                       _ptr(codes), _ptr(sf), _stream(stream)),
            "nvfp4_quantize_experts")
 
 
-def quantize_experts_fp16(x, ldx: int, num_rows: int, K: int, topk: int, expert_idx, dst_row,
-                          num_experts: int, gscale, codes, sf, num_dst_rows: int, stream=None):
-    _check(_lib.nvfp4_quantize_experts_fp16(_ptr(x), ldx, num_rows, K, topk, _ptr(expert_idx),
-                                            _ptr(dst_row), num_experts, _ptr(gscale),
-                                            _ptr(codes), _ptr(sf), num_dst_rows, _stream(stream)),
+def quantize_experts_fp16(x, ldx: int, K: int, src_row, num_src_rows: int, P: int,
+                          expert_offsets, num_experts: int, gscale, codes, sf, stream=None):
+    _check(_lib.nvfp4_quantize_experts_fp16(_ptr(x), ldx, K, _ptr(src_row), num_src_rows, P,
+                                            _ptr(expert_offsets), num_experts, _ptr(gscale),
+                                            _ptr(codes), _ptr(sf), _stream(stream)),
            "nvfp4_quantize_experts_fp16")
+
+
+def quantize_pairs(x, ldx: int, num_rows: int, K: int, topk: int, expert_idx, dst_row,
+                   num_experts: int, gscale, codes, sf, num_dst_rows: int, stream=None):
+    _check(_lib.nvfp4_quantize_pairs(_ptr(x), ldx, num_rows, K, topk, _ptr(expert_idx),
+                                     _ptr(dst_row), num_experts, _ptr(gscale), _ptr(codes),
+                                     _ptr(sf), num_dst_rows, _stream(stream)),
+           "nvfp4_quantize_pairs")
 
 
 def route_topk(logits, num_tokens: int, num_experts: int, k: int, ids, weights, stream=None):
@@ -227,12 +237,20 @@ def moe_forward_w4a16(weights: MoEWeights, x, router_logits, num_tokens: int, k:
                                         _stream(stream)), "nvfp4_moe_forward_w4a16")
 
 
-def quantize_experts_mx(x, ldx: int, num_rows: int, K: int, topk: int, expert_idx, dst_row,
-                        num_experts: int, gscale, codes, sf, num_dst_rows: int, stream=None):
-    _check(_lib.nvfp4_quantize_experts_mx(_ptr(x), ldx, num_rows, K, topk, _ptr(expert_idx),
-                                          _ptr(dst_row), num_experts, _ptr(gscale), _ptr(codes),
-                                          _ptr(sf), num_dst_rows, _stream(stream)),
+def quantize_experts_mx(x, ldx: int, K: int, src_row, num_src_rows: int, P: int,
+                        expert_offsets, num_experts: int, gscale, codes, sf, stream=None):
+    _check(_lib.nvfp4_quantize_experts_mx(_ptr(x), ldx, K, _ptr(src_row), num_src_rows, P,
+                                          _ptr(expert_offsets), num_experts, _ptr(gscale),
+                                          _ptr(codes), _ptr(sf), _stream(stream)),
            "nvfp4_quantize_experts_mx")
+
+
+def quantize_pairs_mx(x, ldx: int, num_rows: int, K: int, topk: int, expert_idx, dst_row,
+                      num_experts: int, gscale, codes, sf, num_dst_rows: int, stream=None):
+    _check(_lib.nvfp4_quantize_pairs_mx(_ptr(x), ldx, num_rows, K, topk, _ptr(expert_idx),
+                                        _ptr(dst_row), num_experts, _ptr(gscale), _ptr(codes),
+                                        _ptr(sf), num_dst_rows, _stream(stream)),
+           "nvfp4_quantize_pairs_mx")
 
 
 def moe_pack_weights_mx(projection: int, codes, sf, num_experts: int, hidden: int, inter: int,

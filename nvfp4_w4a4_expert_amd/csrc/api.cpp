@@ -122,57 +122,92 @@ NVFP4_API nvfp4_status_t nvfp4_validate_scales(const float* input_scale, const u
   return NVFP4_OK;
 }
 
-NVFP4_API nvfp4_status_t nvfp4_quantize_experts(const void* x_bf16, int64_t ldx, int32_t num_rows,
-                                                int32_t K, int32_t topk, const int32_t* expert_idx,
-                                                const int32_t* dst_row, int32_t num_experts,
-                                                const float* gscale, uint8_t* codes, uint8_t* sf,
-                                                int32_t num_dst_rows, nvfp4_stream_t stream) {
-  if (num_rows < 0 || K <= 0 || K % 16 || topk < 1 || num_experts < 1 || num_dst_rows < 0 ||
-      ldx < K || ldx % 8)
+}  // extern "C"
+
+namespace {
+
+// The gather-form quantiser entry points (E4M3 bf16, E4M3 fp16, UE8M0 bf16).
+nvfp4_status_t quantize_gather(const void* x, int64_t ldx, int32_t K, const int32_t* src_row,
+                               int32_t num_src_rows, int32_t P, const int32_t* expert_offsets,
+                               int32_t E, const float* gscale, uint8_t* codes, uint8_t* sf,
+                               nvfp4_stream_t stream, bool fp16, bool mx) {
+  if (P < 0 || K <= 0 || K % (mx ? 32 : 16) || E < 1 || num_src_rows < 0 || ldx < K || ldx % 8)
+    return NVFP4_ERR_INVALID_ARG;
+  if (P == 0) return NVFP4_OK;
+  if (!x || !expert_offsets || !codes || !sf || !aligned(x, 16) || !aligned(codes, 8))
+    return NVFP4_ERR_INVALID_ARG;
+  if (!src_row && num_src_rows < P) return NVFP4_ERR_INVALID_ARG;
+  return device_status(launch_quantize_gather(static_cast<const uint16_t*>(x), ldx, K, src_row, 1,
+                                              num_src_rows, P, expert_offsets, E, gscale, codes,
+                                              sf, static_cast<hipStream_t>(stream), fp16, mx));
+}
+
+// The scatter-form (token-slot pairs) entry points.
+nvfp4_status_t quantize_pairs(const void* x_bf16, int64_t ldx, int32_t num_rows, int32_t K,
+                              int32_t topk, const int32_t* expert_idx, const int32_t* dst_row,
+                              int32_t num_experts, const float* gscale, uint8_t* codes,
+                              uint8_t* sf, int32_t num_dst_rows, nvfp4_stream_t stream, bool mx) {
+  if (num_rows < 0 || K <= 0 || K % (mx ? 32 : 16) || topk < 1 || num_experts < 1 ||
+      num_dst_rows < 0 || ldx < K || ldx % 8)
     return NVFP4_ERR_INVALID_ARG;
   if (num_rows == 0) return NVFP4_OK;
   if (!x_bf16 || !codes || !sf || !aligned(x_bf16, 16) || !aligned(codes, 8))
     return NVFP4_ERR_INVALID_ARG;
   return device_status(launch_quantize(static_cast<const uint16_t*>(x_bf16), ldx, num_rows, K,
                                        topk, expert_idx, dst_row, num_experts, gscale, codes, sf,
-                                       num_dst_rows, static_cast<hipStream_t>(stream)));
+                                       num_dst_rows, static_cast<hipStream_t>(stream), false, mx));
 }
 
-NVFP4_API nvfp4_status_t nvfp4_quantize_experts_fp16(const void* x_fp16, int64_t ldx,
-                                                     int32_t num_rows, int32_t K, int32_t topk,
-                                                     const int32_t* expert_idx,
-                                                     const int32_t* dst_row, int32_t num_experts,
-                                                     const float* gscale, uint8_t* codes,
-                                                     uint8_t* sf, int32_t num_dst_rows,
+}  // namespace
+
+extern "C" {
+
+NVFP4_API nvfp4_status_t nvfp4_quantize_experts(const void* x_bf16, int64_t ldx, int32_t K,
+                                                const int32_t* src_row, int32_t num_src_rows,
+                                                int32_t P, const int32_t* expert_offsets,
+                                                int32_t E, const float* gscale, uint8_t* codes,
+                                                uint8_t* sf, nvfp4_stream_t stream) {
+  return quantize_gather(x_bf16, ldx, K, src_row, num_src_rows, P, expert_offsets, E, gscale,
+                         codes, sf, stream, false, false);
+}
+
+NVFP4_API nvfp4_status_t nvfp4_quantize_experts_fp16(const void* x_fp16, int64_t ldx, int32_t K,
+                                                     const int32_t* src_row, int32_t num_src_rows,
+                                                     int32_t P, const int32_t* expert_offsets,
+                                                     int32_t E, const float* gscale,
+                                                     uint8_t* codes, uint8_t* sf,
                                                      nvfp4_stream_t stream) {
-  if (num_rows < 0 || K <= 0 || K % 16 || topk < 1 || num_experts < 1 || num_dst_rows < 0 ||
-      ldx < K || ldx % 8)
-    return NVFP4_ERR_INVALID_ARG;
-  if (num_rows == 0) return NVFP4_OK;
-  if (!x_fp16 || !codes || !sf || !aligned(x_fp16, 16) || !aligned(codes, 8))
-    return NVFP4_ERR_INVALID_ARG;
-  return device_status(launch_quantize(static_cast<const uint16_t*>(x_fp16), ldx, num_rows, K,
-                                       topk, expert_idx, dst_row, num_experts, gscale, codes, sf,
-                                       num_dst_rows, static_cast<hipStream_t>(stream), true));
+  return quantize_gather(x_fp16, ldx, K, src_row, num_src_rows, P, expert_offsets, E, gscale,
+                         codes, sf, stream, true, false);
 }
 
-NVFP4_API nvfp4_status_t nvfp4_quantize_experts_mx(const void* x_bf16, int64_t ldx,
-                                                   int32_t num_rows, int32_t K, int32_t topk,
-                                                   const int32_t* expert_idx,
-                                                   const int32_t* dst_row, int32_t num_experts,
-                                                   const float* gscale, uint8_t* codes,
-                                                   uint8_t* sf, int32_t num_dst_rows,
-                                                   nvfp4_stream_t stream) {
-  if (num_rows < 0 || K <= 0 || K % 32 || topk < 1 || num_experts < 1 || num_dst_rows < 0 ||
-      ldx < K || ldx % 8)
-    return NVFP4_ERR_INVALID_ARG;
-  if (num_rows == 0) return NVFP4_OK;
-  if (!x_bf16 || !codes || !sf || !aligned(x_bf16, 16) || !aligned(codes, 8))
-    return NVFP4_ERR_INVALID_ARG;
-  return device_status(launch_quantize(static_cast<const uint16_t*>(x_bf16), ldx, num_rows, K,
-                                       topk, expert_idx, dst_row, num_experts, gscale, codes, sf,
-                                       num_dst_rows, static_cast<hipStream_t>(stream), false,
-                                       true));
+NVFP4_API nvfp4_status_t nvfp4_quantize_experts_mx(const void* x_bf16, int64_t ldx, int32_t K,
+                                                   const int32_t* src_row, int32_t num_src_rows,
+                                                   int32_t P, const int32_t* expert_offsets,
+                                                   int32_t E, const float* gscale, uint8_t* codes,
+                                                   uint8_t* sf, nvfp4_stream_t stream) {
+  return quantize_gather(x_bf16, ldx, K, src_row, num_src_rows, P, expert_offsets, E, gscale,
+                         codes, sf, stream, false, true);
+}
+
+NVFP4_API nvfp4_status_t nvfp4_quantize_pairs(const void* x_bf16, int64_t ldx, int32_t num_rows,
+                                              int32_t K, int32_t topk, const int32_t* expert_idx,
+                                              const int32_t* dst_row, int32_t num_experts,
+                                              const float* gscale, uint8_t* codes, uint8_t* sf,
+                                              int32_t num_dst_rows, nvfp4_stream_t stream) {
+  return quantize_pairs(x_bf16, ldx, num_rows, K, topk, expert_idx, dst_row, num_experts, gscale,
+                        codes, sf, num_dst_rows, stream, false);
+}
+
+NVFP4_API nvfp4_status_t nvfp4_quantize_pairs_mx(const void* x_bf16, int64_t ldx,
+                                                 int32_t num_rows, int32_t K, int32_t topk,
+                                                 const int32_t* expert_idx,
+                                                 const int32_t* dst_row, int32_t num_experts,
+                                                 const float* gscale, uint8_t* codes,
+                                                 uint8_t* sf, int32_t num_dst_rows,
+                                                 nvfp4_stream_t stream) {
+  return quantize_pairs(x_bf16, ldx, num_rows, K, topk, expert_idx, dst_row, num_experts, gscale,
+                        codes, sf, num_dst_rows, stream, true);
 }
 
 NVFP4_API nvfp4_status_t nvfp4_route_topk(const float* logits, int32_t num_tokens,

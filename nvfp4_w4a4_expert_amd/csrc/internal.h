@@ -14,6 +14,15 @@ hipError_t launch_quantize(const uint16_t* x, int64_t ldx, int32_t num_rows, int
                            int32_t num_dst_rows, hipStream_t stream, bool fp16_input = false,
                            bool mx = false);
 
+// The quantiser's gather form: destination row p quantises source row
+// src_row[p] / src_div (p when src_row is null) with the SFScaleVal of its
+// expert (offsets[e] <= p < offsets[e+1]).
+hipError_t launch_quantize_gather(const uint16_t* x, int64_t ldx, int32_t K,
+                                  const int32_t* src_row, int32_t src_div, int32_t num_src_rows,
+                                  int32_t P, const int32_t* offsets, int32_t E,
+                                  const float* gscale, uint8_t* codes, uint8_t* sf,
+                                  hipStream_t stream, bool fp16_input = false, bool mx = false);
+
 hipError_t launch_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* ids,
                         float* weights, hipStream_t stream);
 

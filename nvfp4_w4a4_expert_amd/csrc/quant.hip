@@ -119,6 +119,79 @@ __global__ __launch_bounds__(1024) void quantize_experts_kernel(
   }
 }
 
+// Gather form: one workgroup per destination row p (grid.x) and one 16-element
+// block per lane.  Row p belongs to the expert e with offsets[e] <= p <
+// offsets[e+1] (found by a wave-uniform binary search) and quantises source
+// row src_row[p] / src_div of x (row p when src_row is null) with that
+// expert's SFScaleVal.  Rows outside [offsets[0], offsets[E]) and rows whose
+// source row falls outside [0, num_src_rows) are not written.  The row's code
+// bytes and scale bytes are written by one workgroup, contiguously.
+template <bool kS, bool kG, bool kF16, bool kMX>
+__global__ __launch_bounds__(1024) void quantize_gather_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, int32_t nblk, const int32_t* __restrict__ src_row,
+    int32_t src_div, int32_t num_src_rows, const int32_t* __restrict__ offsets, int32_t E,
+    const float* __restrict__ gscale, uint8_t* __restrict__ codes, uint8_t* __restrict__ sf) {
+#pragma clang fp contract(off)
+  const int32_t p = (int32_t)blockIdx.x;
+  const int32_t b = (int32_t)blockIdx.y * (int32_t)blockDim.x + (int32_t)threadIdx.x;
+  if (p < offsets[0] || p >= offsets[E]) return;             // uniform per workgroup
+  int32_t lo = 0, hi = E - 1;                                // last e with offsets[e] <= p
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (offsets[mid] <= p) lo = mid; else hi = mid - 1;
+  }
+  const int32_t s = kS ? src_row[p] : p;
+  if (s < 0) return;
+  const int64_t srow = kS ? (int64_t)(s / src_div) : (int64_t)p;
+  if (srow >= num_src_rows) return;
+  const float gs = kG ? gscale[lo] : 1.0f;
+  const bool on = b < nblk;
+  float xv[16];
+  float a6 = 0.0f;
+  if (on) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + srow * ldx + (int64_t)b * 16);
+    const u32x4 v0 = __builtin_nontemporal_load(src);
+    const u32x4 v1 = __builtin_nontemporal_load(src + 1);
+    if constexpr (kF16) {
+      unpack_f16x8(v0, xv);
+      unpack_f16x8(v1, xv + 8);
+    } else {
+      unpack_bf16x8(v0, xv);
+      unpack_bf16x8(v1, xv + 8);
+    }
+    a6 = absmax16(xv);
+  }
+  if constexpr (kMX) a6 = fmaxf(a6, __shfl_xor(a6, 1, 64));   // the block's other half
+  a6 = a6 / kE2M1Max;
+  const BlockScale bs = kMX ? block_scale_ue8m0(a6, gs) : block_scale(a6, gs);
+  if (on) {
+    uint2 w;
+    w.x = encode8(xv, bs.inv);
+    w.y = encode8(xv + 8, bs.inv);
+    *reinterpret_cast<uint2*>(codes + (int64_t)p * nblk * 8 + (int64_t)b * 8) = w;
+  }
+  const bool sf_words = (reinterpret_cast<uintptr_t>(sf) & 3) == 0 && (kMX ? nblk % 8 : nblk % 4) == 0;
+  if (sf_words) {
+    uint32_t v = bs.sf;
+    if constexpr (kMX) {
+      v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false) << 8;
+      v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x104, 0xF, 0xF, false) << 16;
+      if (on && (b & 7) == 0)
+        *reinterpret_cast<uint32_t*>(sf + (int64_t)p * (nblk / 2) + b / 2) = v;
+    } else {
+      v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false) << 8;
+      v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false) << 16;
+      if (on && (b & 3) == 0) *reinterpret_cast<uint32_t*>(sf + (int64_t)p * nblk + b) = v;
+    }
+  } else if (on) {
+    if constexpr (kMX) {
+      if ((b & 1) == 0) sf[(int64_t)p * (nblk / 2) + b / 2] = (uint8_t)bs.sf;
+    } else {
+      sf[(int64_t)p * nblk + b] = (uint8_t)bs.sf;
+    }
+  }
+}
+
 namespace {
 
 template <bool kF16, bool kMX>
@@ -172,6 +245,54 @@ hipError_t launch_quantize(const uint16_t* x, int64_t ldx, int32_t num_rows, int
     launch_quantize_variant<false, false>(variant, grid, threads, stream, x, ldx, num_rows, nblk,
                                           topk, expert_idx, dst_row, num_experts, gscale, codes,
                                           sf, num_dst_rows);
+  return hipGetLastError();
+}
+
+namespace {
+
+template <bool kF16, bool kMX>
+void launch_gather_variant(int variant, dim3 grid, int32_t threads, hipStream_t stream,
+                           const uint16_t* x, int64_t ldx, int32_t nblk, const int32_t* src_row,
+                           int32_t src_div, int32_t num_src_rows, const int32_t* offsets,
+                           int32_t E, const float* gscale, uint8_t* codes, uint8_t* sf) {
+#define NVFP4_GATHER_CASE(v, ks, kg)                                                            \
+  case v:                                                                                       \
+    hipLaunchKernelGGL((quantize_gather_kernel<ks, kg, kF16, kMX>), grid, dim3(threads), 0,     \
+                       stream, x, ldx, nblk, src_row, src_div, num_src_rows, offsets, E,        \
+                       gscale, codes, sf);                                                      \
+    break;
+  switch (variant) {
+    NVFP4_GATHER_CASE(0, false, false)
+    NVFP4_GATHER_CASE(1, false, true)
+    NVFP4_GATHER_CASE(2, true, false)
+    NVFP4_GATHER_CASE(3, true, true)
+  }
+#undef NVFP4_GATHER_CASE
+}
+
+}  // namespace
+
+hipError_t launch_quantize_gather(const uint16_t* x, int64_t ldx, int32_t K,
+                                  const int32_t* src_row, int32_t src_div, int32_t num_src_rows,
+                                  int32_t P, const int32_t* offsets, int32_t E,
+                                  const float* gscale, uint8_t* codes, uint8_t* sf,
+                                  hipStream_t stream, bool fp16_input, bool mx) {
+  const int32_t nblk = K / 16;
+  if ((int64_t)P * nblk == 0) return hipSuccess;
+  // 64-lane wavefronts covering the row's blocks, at most 1024 threads per
+  // workgroup (1024 is even, so a 32-element block never straddles two)
+  const int32_t threads = min(1024, (nblk + 63) / 64 * 64);
+  const dim3 grid((uint32_t)P, (uint32_t)((nblk + threads - 1) / threads));
+  const int variant = (src_row ? 2 : 0) | (gscale ? 1 : 0);
+  if (mx)
+    launch_gather_variant<false, true>(variant, grid, threads, stream, x, ldx, nblk, src_row,
+                                       src_div, num_src_rows, offsets, E, gscale, codes, sf);
+  else if (fp16_input)
+    launch_gather_variant<true, false>(variant, grid, threads, stream, x, ldx, nblk, src_row,
+                                       src_div, num_src_rows, offsets, E, gscale, codes, sf);
+  else
+    launch_gather_variant<false, false>(variant, grid, threads, stream, x, ldx, nblk, src_row,
+                                        src_div, num_src_rows, offsets, E, gscale, codes, sf);
   return hipGetLastError();
 }
 

@@ -21,9 +21,6 @@ import torch
 
 from . import _lib
 
-NVFP4_RANGE = np.float32(6.0 * 448.0)   # E2M1 max x E4M3 max
-
-
 class BadScaleError(ValueError):
     """Per-expert activation scales failed the load-time check."""
 
@@ -194,27 +191,28 @@ class NVFP4W4A16MoELayer(NVFP4MoELayer):
 # --- producing a layer with the library's kernels ----------------------------
 
 def quantize_expert_weights(w: torch.Tensor, stream=None, mx: bool = False):
-    """Static NVFP4 quantisation of bf16 expert weights [E, N, K] on the GPU:
-    weight_scale_2[e] = fl32(max|W[e]| / 2688), SFScaleVal = fl32(1 / that),
-    then the per-expert quantiser (UE8M0 scales per 32 elements when mx).
+    """Static NVFP4 quantisation of bf16 expert weights [E, N, K] on the GPU,
+    with the library's kernels: weight_scale_2[e] = fl32(max|W[e]| / 2688)
+    (the calibration pass over each expert's N rows), the load-time check and
+    reciprocal of it (SFScaleVal), then the per-expert quantiser over the
+    expert-grouped rows (UE8M0 scales per 32 elements when mx).
     Returns (codes, sf, scale2) tensors."""
     E, N, K = (int(s) for s in w.shape)
     dev = w.device
     flat = w.reshape(E * N, K)
     offsets = torch.arange(0, E * N + 1, N, dtype=torch.int32, device=dev)
-    amax = torch.empty(E, dtype=torch.float32, device=dev)
-    _lib.expert_absmax(flat, K, K, None, 1, offsets, E, E * N, amax, stream)
-    scale2 = (amax.cpu().numpy().astype(np.float32) / NVFP4_RANGE).astype(np.float32)
-    st, gs, slots, _ = _lib.validate_scales(scale2)
+    scale2 = torch.empty(E, dtype=torch.float32, device=dev)
+    written = torch.empty(E, dtype=torch.uint8, device=dev)
+    _lib.calibrate_input_scales(flat, K, K, None, 1, offsets, E, E * N, scale2, written, stream)
+    st, gs, slots, _ = _lib.validate_scales(scale2.cpu().numpy(), written.cpu().numpy())
     if st != _lib.OK:
         raise BadScaleError("weight_scale_2", slots)
-    expert_of_row = torch.arange(E, dtype=torch.int32, device=dev).repeat_interleave(N)
     codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev)
     sf = torch.empty((E, N, K // (32 if mx else 16)), dtype=torch.uint8, device=dev)
     quant = _lib.quantize_experts_mx if mx else _lib.quantize_experts
-    quant(flat, K, E * N, K, 1, expert_of_row, None, E, torch.from_numpy(gs).to(dev), codes, sf,
-          E * N, stream)
-    return codes, sf, torch.from_numpy(scale2).to(dev)
+    quant(flat, K, K, None, E * N, E * N, offsets, E, torch.from_numpy(gs).to(dev), codes, sf,
+          stream)
+    return codes, sf, scale2
 
 
 @dataclass

@@ -22,6 +22,7 @@
 static std::vector<std::string> g_calls;
 static int g_quant_mx = -1, g_gemm1_mode = -1, g_gemm2_mode = -1;
 static int32_t g_gemm1_P = -1, g_quant_dst_rows = -1;
+static int g_gather_src_div = -1;
 
 namespace nvfp4 {
 hipError_t launch_quantize(const uint16_t*, int64_t, int32_t, int32_t, int32_t, const int32_t*,
@@ -30,6 +31,14 @@ hipError_t launch_quantize(const uint16_t*, int64_t, int32_t, int32_t, int32_t, 
   g_calls.push_back("quantize");
   g_quant_mx = mx;
   g_quant_dst_rows = num_dst_rows;
+  return hipSuccess;
+}
+hipError_t launch_quantize_gather(const uint16_t*, int64_t, int32_t, const int32_t*,
+                                  int32_t src_div, int32_t, int32_t, const int32_t*, int32_t,
+                                  const float*, uint8_t*, uint8_t*, hipStream_t, bool, bool mx) {
+  g_calls.push_back("quantize_gather");
+  g_quant_mx = mx;
+  g_gather_src_div = src_div;
   return hipSuccess;
 }
 hipError_t launch_route(const float*, int32_t, int32_t, int32_t, int32_t*, float*, hipStream_t) {
@@ -259,16 +268,40 @@ static void entry_point_checks() {
   uint8_t* codes = (uint8_t*)b.get(4096);
   uint8_t* sf = (uint8_t*)b.get(4096);
   g_calls.clear();
-  CHECK(nvfp4_quantize_experts(x, 24, 1, 24, 1, nullptr, nullptr, 1, nullptr, codes, sf, 1,
-                               nullptr) == NVFP4_ERR_INVALID_ARG);  // K % 16
-  CHECK(nvfp4_quantize_experts_mx(x, 48, 1, 48, 1, nullptr, nullptr, 1, nullptr, codes, sf, 1,
+  int32_t* offs = (int32_t*)b.get(64);
+  int32_t* rows = (int32_t*)b.get(64);
+  // scatter (pairs) form
+  CHECK(nvfp4_quantize_pairs(x, 24, 1, 24, 1, nullptr, nullptr, 1, nullptr, codes, sf, 1,
+                             nullptr) == NVFP4_ERR_INVALID_ARG);  // K % 16
+  CHECK(nvfp4_quantize_pairs_mx(x, 48, 1, 48, 1, nullptr, nullptr, 1, nullptr, codes, sf, 1,
+                                nullptr) == NVFP4_ERR_INVALID_ARG);  // K % 32
+  CHECK(nvfp4_quantize_pairs((char*)x + 8, 16, 1, 16, 1, nullptr, nullptr, 1, nullptr, codes,
+                             sf, 1, nullptr) == NVFP4_ERR_INVALID_ARG);  // x alignment
+  // gather form
+  CHECK(nvfp4_quantize_experts(x, 24, 24, rows, 4, 2, offs, 1, nullptr, codes, sf, nullptr) ==
+        NVFP4_ERR_INVALID_ARG);  // K % 16
+  CHECK(nvfp4_quantize_experts_mx(x, 48, 48, rows, 4, 2, offs, 1, nullptr, codes, sf,
                                   nullptr) == NVFP4_ERR_INVALID_ARG);  // K % 32
-  CHECK(nvfp4_quantize_experts((char*)x + 8, 16, 1, 16, 1, nullptr, nullptr, 1, nullptr, codes,
-                               sf, 1, nullptr) == NVFP4_ERR_INVALID_ARG);  // x alignment
+  CHECK(nvfp4_quantize_experts(x, 16, 16, rows, 4, 2, nullptr, 1, nullptr, codes, sf, nullptr) ==
+        NVFP4_ERR_INVALID_ARG);  // offsets required
+  CHECK(nvfp4_quantize_experts(x, 16, 16, nullptr, 1, 2, offs, 1, nullptr, codes, sf, nullptr) ==
+        NVFP4_ERR_INVALID_ARG);  // identity rows need num_src_rows >= P
+  CHECK(nvfp4_quantize_experts_fp16((char*)x + 8, 16, 16, rows, 4, 2, offs, 1, nullptr, codes,
+                                    sf, nullptr) == NVFP4_ERR_INVALID_ARG);  // x alignment
+  CHECK(nvfp4_quantize_experts(x, 16, 16, rows, 4, 2, offs, 0, nullptr, codes, sf, nullptr) ==
+        NVFP4_ERR_INVALID_ARG);  // no experts
   CHECK(g_calls.empty());
-  CHECK(nvfp4_quantize_experts(x, 32, 2, 32, 1, nullptr, nullptr, 1, nullptr, codes, sf, 2,
-                               nullptr) == NVFP4_OK);
-  CHECK(g_calls.size() == 1 && g_quant_mx == 0);
+  CHECK(nvfp4_quantize_experts(nullptr, 16, 16, nullptr, 0, 0, nullptr, 1, nullptr, nullptr,
+                               nullptr, nullptr) == NVFP4_OK);  // P == 0 is a no-op
+  CHECK(g_calls.empty());
+  CHECK(nvfp4_quantize_pairs(x, 32, 2, 32, 1, nullptr, nullptr, 1, nullptr, codes, sf, 2,
+                             nullptr) == NVFP4_OK);
+  CHECK(g_calls.size() == 1 && g_calls[0] == "quantize" && g_quant_mx == 0);
+  g_calls.clear();
+  CHECK(nvfp4_quantize_experts_mx(x, 64, 64, rows, 4, 2, offs, 1, nullptr, codes, sf, nullptr) ==
+        NVFP4_OK);
+  CHECK(g_calls.size() == 1 && g_calls[0] == "quantize_gather" && g_quant_mx == 1 &&
+        g_gather_src_div == 1);
   CHECK(nvfp4_route_topk((const float*)x, 4, 2000, 8, (int32_t*)codes, (float*)sf, nullptr) ==
         NVFP4_ERR_UNSUPPORTED);
   CHECK(nvfp4_route_topk((const float*)x, 4, 8, 9, (int32_t*)codes, (float*)sf, nullptr) ==
@@ -281,7 +314,7 @@ static void entry_point_checks() {
         NVFP4_ERR_UNSUPPORTED);  // hidden % 256 in the UE8M0 mode
   size_t n = 0;
   CHECK(nvfp4_moe_workspace_size(-1, 8, nullptr, &n) == NVFP4_ERR_INVALID_ARG);
-  for (int s = 0; s <= 5; ++s) CHECK(strlen(nvfp4_status_string((nvfp4_status_t)s)) > 0);
+  for (int s = 0; s <= 6; ++s) CHECK(strlen(nvfp4_status_string((nvfp4_status_t)s)) > 0);
   CHECK(strstr(nvfp4_status_string((nvfp4_status_t)99), "unknown") != nullptr);
   CHECK(nvfp4_abi_version() == NVFP4_ABI_VERSION);
 }

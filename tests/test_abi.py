@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
                  "nvfp4_quantize_experts_fp16", "nvfp4_calibrate_input_scales",
                  "nvfp4_moe_forward_w4a16", "nvfp4_moe_workspace_size_w4a16",
                  "nvfp4_quantize_experts_mx", "nvfp4_moe_pack_weights_mx",
-                 "nvfp4_moe_forward_mx", "nvfp4_moe_forward_noalloc"]:
+                 "nvfp4_moe_forward_mx", "nvfp4_moe_forward_noalloc",
+                 "nvfp4_quantize_pairs", "nvfp4_quantize_pairs_mx"]:
         assert name in syms
 
 
@@ -49,7 +50,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = _lib()
-    assert L.abi_version() == 5
+    assert L.abi_version() == 6
     for s in range(7):
         assert L.status_string(s)
     assert "unknown" in L.status_string(99)
@@ -102,14 +103,23 @@ def test_validator_rejects_bad_args():
 def test_host_argument_checks_return_before_enqueue():
     L = _lib()
     f = L._lib
-    # K not a multiple of 16
-    assert f.nvfp4_quantize_experts(16, 24, 1, 24, 1, None, None, 1, None, 16, 16, 1, None) \
+    # K not a multiple of 16 (both forms)
+    assert f.nvfp4_quantize_pairs(16, 24, 1, 24, 1, None, None, 1, None, 16, 16, 1, None) \
+        == L.ERR_INVALID_ARG
+    assert f.nvfp4_quantize_experts(16, 24, 24, 16, 4, 1, 16, 1, None, 16, 16, None) \
         == L.ERR_INVALID_ARG
     # misaligned x
-    assert f.nvfp4_quantize_experts(8, 16, 1, 16, 1, None, None, 1, None, 16, 16, 1, None) \
+    assert f.nvfp4_quantize_pairs(8, 16, 1, 16, 1, None, None, 1, None, 16, 16, 1, None) \
+        == L.ERR_INVALID_ARG
+    assert f.nvfp4_quantize_experts(8, 16, 16, 16, 4, 1, 16, 1, None, 16, 16, None) \
+        == L.ERR_INVALID_ARG
+    # the gather form needs the expert offsets
+    assert f.nvfp4_quantize_experts(16, 16, 16, 16, 4, 1, None, 1, None, 16, 16, None) \
         == L.ERR_INVALID_ARG
     # zero rows is a no-op that never touches the device
-    assert f.nvfp4_quantize_experts(None, 16, 0, 16, 1, None, None, 1, None, None, None, 0, None) \
+    assert f.nvfp4_quantize_pairs(None, 16, 0, 16, 1, None, None, 1, None, None, None, 0, None) \
+        == L.OK
+    assert f.nvfp4_quantize_experts(None, 16, 16, None, 0, 0, None, 1, None, None, None, None) \
         == L.OK
     # router: k > E, E too large
     assert f.nvfp4_route_topk(16, 4, 4, 5, 16, 16, None) == L.ERR_INVALID_ARG
@@ -186,7 +196,9 @@ def test_ue8m0_mode_host_checks():
     assert f.nvfp4_moe_forward_mx(ctypes.byref(w), fake, fake, 4, 2, None, fake, fake, 1 << 30,
                                   None, None) == L.ERR_UNSUPPORTED
     # K not a multiple of 32 in the UE8M0 quantiser
-    assert f.nvfp4_quantize_experts_mx(16, 48, 1, 48, 1, None, None, 1, None, 16, 16, 1, None) \
+    assert f.nvfp4_quantize_pairs_mx(16, 48, 1, 48, 1, None, None, 1, None, 16, 16, 1, None) \
+        == L.ERR_INVALID_ARG
+    assert f.nvfp4_quantize_experts_mx(16, 48, 48, 16, 4, 1, 16, 1, None, 16, 16, None) \
         == L.ERR_INVALID_ARG
     # the activation scales are required, as in the E4M3 mode
     w = L.MoEWeights(*([fake] * 6), 0, 0, 0, 0, 4, 256, 128)

@@ -20,6 +20,7 @@ GS_SET = np.array([1.0, 1.0 / 3.0, 448.0 / 6.0, 2688.0, 1e-3, 3.0e38, 0.7071, 12
 
 
 def _gpu_quantize_mx(x_bits, K, topk, expert_idx, dst_row, gscale, num_dst_rows):
+    """nvfp4_quantize_pairs_mx: token rows scattered to their destination rows."""
     import torch
     from nvfp4_w4a4_expert_amd import _lib as L
     from nvfp4_w4a4_expert_amd import moe as M
@@ -29,9 +30,24 @@ def _gpu_quantize_mx(x_bits, K, topk, expert_idx, dst_row, gscale, num_dst_rows)
     E = 1 if gscale is None else len(gscale)
     codes = torch.full((num_dst_rows, K // 2), 0xAB, dtype=torch.uint8, device="cuda")
     sf = torch.full((num_dst_rows, K // 32), 0xCD, dtype=torch.uint8, device="cuda")
-    L.quantize_experts_mx(x, x_bits.shape[1], R, K, topk, dev(expert_idx, np.int32),
-                          dev(dst_row, np.int32), E, dev(gscale, np.float32), codes, sf,
-                          num_dst_rows)
+    L.quantize_pairs_mx(x, x_bits.shape[1], R, K, topk, dev(expert_idx, np.int32),
+                        dev(dst_row, np.int32), E, dev(gscale, np.float32), codes, sf,
+                        num_dst_rows)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), sf.cpu().numpy()
+
+
+def _gpu_quantize_mx_gather(x_bits, K, src_row, offsets, gscale, P):
+    """nvfp4_quantize_experts_mx: grouped output rows gathered from x."""
+    import torch
+    from nvfp4_w4a4_expert_amd import _lib as L
+    from nvfp4_w4a4_expert_amd import moe as M
+    dev = lambda a, t: None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=t)).cuda()
+    codes = torch.full((P, K // 2), 0xAB, dtype=torch.uint8, device="cuda")
+    sf = torch.full((P, K // 32), 0xCD, dtype=torch.uint8, device="cuda")
+    L.quantize_experts_mx(M.bf16_tensor(x_bits), x_bits.shape[1], K, dev(src_row, np.int32),
+                          x_bits.shape[0], P, dev(offsets, np.int32), len(offsets) - 1,
+                          dev(gscale, np.float32), codes, sf)
     torch.cuda.synchronize()
     return codes.cpu().numpy(), sf.cpu().numpy()
 
@@ -47,6 +63,13 @@ def test_mx_quantizer_every_bf16_pattern_every_scale():
     codes, sf = _gpu_quantize_mx(x, 256, 1, expert, None, GS_SET, R)
     oc, osf = OX.quantize_experts(x, expert, GS_SET)
     assert (osf == 1).any() and (osf == 254).any()         # both clamps exercised
+    assert np.array_equal(sf, osf)
+    assert np.array_equal(codes, oc)
+    order = np.argsort(expert, kind="stable")
+    offsets = np.zeros(GS_SET.size + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(np.bincount(expert, minlength=GS_SET.size))
+    codes, sf = _gpu_quantize_mx_gather(x, 256, order, offsets, GS_SET, R)
+    oc, osf = OX.quantize_experts(x[order], expert[order], GS_SET)
     assert np.array_equal(sf, osf)
     assert np.array_equal(codes, oc)
 
@@ -66,6 +89,9 @@ def test_mx_quantizer_routed_rows_and_ragged_width():
     gs = (10.0 ** rng.uniform(-2, 3, E)).astype(np.float32)
     codes, sf = _gpu_quantize_mx(x, K, k, ids, inv, gs, T * k)
     oc, osf = OX.quantize_experts(x[src // k], OM.row_experts(offsets), gs)
+    assert np.array_equal(sf, osf)
+    assert np.array_equal(codes, oc)
+    codes, sf = _gpu_quantize_mx_gather(x, K, src // k, offsets, gs, T * k)
     assert np.array_equal(sf, osf)
     assert np.array_equal(codes, oc)
 

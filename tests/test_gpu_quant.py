@@ -1,5 +1,6 @@
-"""GPU parity of nvfp4_quantize_experts against the oracle quantiser:
-packed E2M1 codes and E4M3 scales must be bit-exact."""
+"""GPU parity of the quantiser against the oracle quantiser, in both its
+forms (nvfp4_quantize_experts over expert-grouped rows, nvfp4_quantize_pairs
+fused with the regrouping): packed E2M1 codes and E4M3 scales bit-exact."""
 import numpy as np
 import pytest
 
@@ -17,22 +18,51 @@ def _torch():
     return torch
 
 
-def _gpu_quantize(x_bits, K, topk, expert_idx, dst_row, gscale, num_dst_rows, fp16=False):
+def _dev(a, dtype):
+    torch = _torch()
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=dtype)).cuda()
+
+
+def _gpu_quantize(x_bits, K, topk, expert_idx, dst_row, gscale, num_dst_rows):
+    """nvfp4_quantize_pairs: token rows scattered to their destination rows."""
     torch = _torch()
     from nvfp4_w4a4_expert_amd import _lib as L
     from nvfp4_w4a4_expert_amd import moe as M
     R = x_bits.shape[0]
-    x = M.bf16_tensor(x_bits)
-    ei = None if expert_idx is None else torch.from_numpy(np.ascontiguousarray(expert_idx, dtype=np.int32)).cuda()
-    dr = None if dst_row is None else torch.from_numpy(np.ascontiguousarray(dst_row, dtype=np.int32)).cuda()
-    gs = None if gscale is None else torch.from_numpy(np.ascontiguousarray(gscale, dtype=np.float32)).cuda()
     E = 1 if gscale is None else len(gscale)
     codes = torch.full((num_dst_rows, K // 2), 0xAB, dtype=torch.uint8, device="cuda")
     sf = torch.full((num_dst_rows, K // 16), 0xCD, dtype=torch.uint8, device="cuda")
-    fn = L.quantize_experts_fp16 if fp16 else L.quantize_experts
-    fn(x, x_bits.shape[1], R, K, topk, ei, dr, E, gs, codes, sf, num_dst_rows)
+    L.quantize_pairs(M.bf16_tensor(x_bits), x_bits.shape[1], R, K, topk,
+                     _dev(expert_idx, np.int32), _dev(dst_row, np.int32), E,
+                     _dev(gscale, np.float32), codes, sf, num_dst_rows)
     torch.cuda.synchronize()
     return codes.cpu().numpy(), sf.cpu().numpy()
+
+
+def _gpu_quantize_gather(x_bits, K, src_row, offsets, gscale, P, fp16=False, num_src_rows=None):
+    """nvfp4_quantize_experts(_fp16): grouped output rows gathered from x."""
+    torch = _torch()
+    from nvfp4_w4a4_expert_amd import _lib as L
+    from nvfp4_w4a4_expert_amd import moe as M
+    E = len(offsets) - 1
+    x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).cuda()
+    codes = torch.full((P, K // 2), 0xAB, dtype=torch.uint8, device="cuda")
+    sf = torch.full((P, K // 16), 0xCD, dtype=torch.uint8, device="cuda")
+    fn = L.quantize_experts_fp16 if fp16 else L.quantize_experts
+    n_src = x_bits.shape[0] if num_src_rows is None else num_src_rows
+    fn(x, x_bits.shape[1], K, _dev(src_row, np.int32), n_src, P, _dev(offsets, np.int32), E,
+       _dev(gscale, np.float32), codes, sf)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), sf.cpu().numpy()
+
+
+def _grouped(expert, E):
+    """Rows grouped by expert (stable): source row of each grouped row, the
+    expert offsets and each grouped row's expert."""
+    order = np.argsort(expert, kind="stable")
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(np.bincount(expert, minlength=E))
+    return order.astype(np.int32), offsets, np.asarray(expert)[order]
 
 
 GS_SET = np.array([1.0, 1.0 / 3.0, 448.0 / 6.0, 2688.0, 1e-3, 3.0e38, 0.7071, 12345.678,
@@ -56,8 +86,15 @@ def test_every_bf16_pattern_every_scale():
     R = x.shape[0]
     E = GS_SET.size
     expert = np.arange(R, dtype=np.int32) % E
+    # the pairs form, one destination per row
     codes, sf = _gpu_quantize(x, 256, 1, expert, None, GS_SET, R)
     oc, osf = OQ.quantize_experts(x, expert, GS_SET)
+    assert np.array_equal(sf, osf)
+    assert np.array_equal(codes, oc)
+    # the gather form over the rows grouped by expert
+    src, offsets, rexp = _grouped(expert, E)
+    codes, sf = _gpu_quantize_gather(x, 256, src, offsets, GS_SET, R)
+    oc, osf = OQ.quantize_experts(x[src], rexp, GS_SET)
     assert np.array_equal(sf, osf)
     assert np.array_equal(codes, oc)
 
@@ -73,28 +110,44 @@ def test_every_fp16_pattern_every_scale():
     x = np.concatenate([a[:a.size // 256 * 256].reshape(-1, 256) for a in arr])
     R = x.shape[0]
     expert = np.arange(R, dtype=np.int32) % GS_SET.size
-    codes, sf = _gpu_quantize(x, 256, 1, expert, None, GS_SET, R, fp16=True)
-    oc, osf = OQ.quantize_experts(x, expert, GS_SET, fp16=True)
+    src, offsets, rexp = _grouped(expert, GS_SET.size)
+    codes, sf = _gpu_quantize_gather(x, 256, src, offsets, GS_SET, R, fp16=True)
+    oc, osf = OQ.quantize_experts(x[src], rexp, GS_SET, fp16=True)
     assert np.array_equal(sf, osf)
     assert np.array_equal(codes, oc)
 
 
-def test_fp16_topk_scatter_ragged():
+def test_fp16_routed_rows_ragged():
+    """fp16 rows of varied magnitude routed top-4 of 6 experts: the grouped
+    rows gather token t = src_pair / k; a row width of 13 blocks."""
     rng = np.random.default_rng(6)
     T, K, k, E = 29, 208, 4, 6
     x = (rng.standard_normal((T, K)) * np.exp(rng.uniform(-6, 6, (T, 1)))).astype(np.float16)
     x_bits = x.view(np.uint16)
     ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
     gs = np.exp(rng.uniform(-3, 6, E)).astype(np.float32)
+    offsets, src, inv = OM.permute(ids, E)
     P = T * k
-    dst = rng.permutation(P).astype(np.int32)
-    codes, sf = _gpu_quantize(x_bits, K, k, ids.reshape(-1), dst, gs, P, fp16=True)
-    src_tok = np.empty(P, dtype=np.int64)
-    src_tok[dst] = np.arange(P) // k
-    row_exp = np.empty(P, dtype=np.int64)
-    row_exp[dst] = ids.reshape(-1)
-    oc, osf = OQ.quantize_experts(x_bits[src_tok], row_exp, gs, fp16=True)
+    codes, sf = _gpu_quantize_gather(x_bits, K, src // k, offsets, gs, P, fp16=True)
+    oc, osf = OQ.quantize_experts(x_bits[src // k], OM.row_experts(offsets), gs, fp16=True)
     assert np.array_equal(codes, oc) and np.array_equal(sf, osf)
+
+
+def test_gather_skips_rows_without_a_source_or_an_expert():
+    """Output rows whose source row is negative or past the last source row,
+    and rows outside [offsets[0], offsets[E]), are left untouched."""
+    rng = np.random.default_rng(8)
+    x = S.f32_to_bf16_bits(rng.standard_normal((6, 48)).astype(np.float32))
+    src = np.array([0, -1, 5, 6, 2, 3, 1, 4], dtype=np.int32)      # -1 and 6 have no source
+    offsets = np.array([1, 4, 7], dtype=np.int32)                 # rows 0 and 7 have no expert
+    gs = np.array([0.5, 3.0], dtype=np.float32)
+    codes, sf = _gpu_quantize_gather(x, 48, src, offsets, gs, 8)
+    written = [2, 4, 5, 6]
+    rexp = np.array([0, 1, 1, 1])
+    oc, osf = OQ.quantize_experts(x[src[written]], rexp, gs)
+    assert np.array_equal(codes[written], oc) and np.array_equal(sf[written], osf)
+    for r in (0, 1, 3, 7):
+        assert np.all(codes[r] == 0xAB) and np.all(sf[r] == 0xCD)
 
 
 def test_topk_scatter_and_ragged_blocks():
@@ -119,6 +172,8 @@ def test_null_scale_means_unit_scale():
     x = S.f32_to_bf16_bits(rng.standard_normal((8, 64)).astype(np.float32) * 300)
     codes, sf = _gpu_quantize(x, 64, 1, None, None, None, 8)
     oc, osf = OQ.quantize_experts(x, np.zeros(8, dtype=np.int64), None)
+    assert np.array_equal(codes, oc) and np.array_equal(sf, osf)
+    codes, sf = _gpu_quantize_gather(x, 64, None, np.array([0, 3, 8], dtype=np.int32), None, 8)
     assert np.array_equal(codes, oc) and np.array_equal(sf, osf)
 
 
@@ -151,6 +206,9 @@ def test_quantizer_workload_full_size():
     oc, osf = OQ.quantize_experts(x[src // w.k], OM.row_experts(offsets), gs)
     assert np.array_equal(sf, osf)
     assert np.array_equal(codes, oc)
+    codes, sf = _gpu_quantize_gather(x, w.H, src // w.k, offsets, gs, w.P)
+    assert np.array_equal(sf, osf)
+    assert np.array_equal(codes, oc)
     assert np.count_nonzero(osf == 0x7E) > 0
     assert np.count_nonzero((OF.unpack_nibbles(oc) & 7) == 7) > 0
 
@@ -159,7 +217,8 @@ def test_zero_rows_is_noop():
     torch = _torch()
     from nvfp4_w4a4_expert_amd import _lib as L
     codes = torch.full((1, 8), 7, dtype=torch.uint8, device="cuda")
-    L.quantize_experts(None, 16, 0, 16, 1, None, None, 1, None, codes, codes, 0)
+    L.quantize_pairs(None, 16, 0, 16, 1, None, None, 1, None, codes, codes, 0)
+    L.quantize_experts(None, 16, 16, None, 0, 0, None, 1, None, codes, codes)
     torch.cuda.synchronize()
     assert codes.cpu().numpy().tolist() == [[7] * 8]
 
@@ -249,14 +308,22 @@ def test_scale_words_and_byte_fallback(mx, blocks, offset):
     codes = torch.full((P, K // 2), 0xAB, dtype=torch.uint8, device="cuda")
     sf_buf = torch.full((P * (K // blk) + 8,), 0xCD, dtype=torch.uint8, device="cuda")
     sf = sf_buf[offset:offset + P * (K // blk)]
-    fn = L.quantize_experts_mx if mx else L.quantize_experts
     dev = lambda a, t: torch.from_numpy(np.ascontiguousarray(a, dtype=t)).cuda()
-    fn(M.bf16_tensor(x), K, T, K, k, dev(ids, np.int32), dev(inv, np.int32), E, dev(gs, np.float32),
-       codes, sf, P)
-    torch.cuda.synchronize()
     Q = OX if mx else OQ
     oc, osf = Q.quantize_experts(x[src // k], OM.row_experts(offsets), gs)
-    assert np.array_equal(sf.cpu().numpy().reshape(P, K // blk), osf)
-    assert np.array_equal(codes.cpu().numpy(), oc)
-    rest = sf_buf.cpu().numpy()
-    assert np.all(rest[:offset] == 0xCD) and np.all(rest[offset + P * (K // blk):] == 0xCD)
+    for form in ("pairs", "gather"):
+        codes.fill_(0xAB)
+        sf_buf.fill_(0xCD)
+        if form == "pairs":
+            fn = L.quantize_pairs_mx if mx else L.quantize_pairs
+            fn(M.bf16_tensor(x), K, T, K, k, dev(ids, np.int32), dev(inv, np.int32), E,
+               dev(gs, np.float32), codes, sf, P)
+        else:
+            fn = L.quantize_experts_mx if mx else L.quantize_experts
+            fn(M.bf16_tensor(x), K, K, dev(src // k, np.int32), T, P, dev(offsets, np.int32), E,
+               dev(gs, np.float32), codes, sf)
+        torch.cuda.synchronize()
+        assert np.array_equal(sf.cpu().numpy().reshape(P, K // blk), osf), form
+        assert np.array_equal(codes.cpu().numpy(), oc), form
+        rest = sf_buf.cpu().numpy()
+        assert np.all(rest[:offset] == 0xCD) and np.all(rest[offset + P * (K // blk):] == 0xCD)
