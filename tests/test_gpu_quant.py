@@ -177,12 +177,15 @@ def test_null_scale_means_unit_scale():
     assert np.array_equal(codes, oc) and np.array_equal(sf, osf)
 
 
-def test_out_of_range_destinations_are_skipped():
+@pytest.mark.parametrize("K", [32, 64])
+def test_out_of_range_destinations_are_skipped(K):
+    """Pairs whose destination row or expert is out of range are skipped (K = 64
+    runs the layer's specialised kernel, K = 32 the general one)."""
     rng = np.random.default_rng(3)
-    x = S.f32_to_bf16_bits(rng.standard_normal((4, 32)).astype(np.float32))
+    x = S.f32_to_bf16_bits(rng.standard_normal((4, K)).astype(np.float32))
     dst = np.array([0, 7, -1, 2], dtype=np.int32)               # 7 and -1 out of range
     expert = np.array([0, 0, 0, 5], dtype=np.int32)             # 5 out of range
-    codes, sf = _gpu_quantize(x, 32, 1, expert, dst, np.ones(2, dtype=np.float32), 4)
+    codes, sf = _gpu_quantize(x, K, 1, expert, dst, np.ones(2, dtype=np.float32), 4)
     oc, osf = OQ.quantize_experts(x[[0]], np.array([0]), np.ones(1, dtype=np.float32))
     assert np.array_equal(codes[0], oc[0]) and np.array_equal(sf[0], osf[0])
     assert np.all(codes[1:] == 0xAB) and np.all(sf[1:] == 0xCD)
