@@ -645,10 +645,10 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
           if (row < rows) {
             const int64_t p = row0 + row;
             if (prm.c1_dbg) {
-              prm.c1_dbg[c_offset(row0, row, 2 * I, hbase + col, 0)] = gv;
-              prm.c1_dbg[c_offset(row0, row, 2 * I, I + hbase + col, 0)] = uv;
+              prm.c1_dbg[row_major(p, 2 * I, hbase + col)] = gv;
+              prm.c1_dbg[row_major(p, 2 * I, I + hbase + col)] = uv;
             }
-            if (prm.h_dbg) prm.h_dbg[c_offset(row0, row, I, hbase + col, 0)] = (uint16_t)hb;
+            if (prm.h_dbg) prm.h_dbg[row_major(p, I, hbase + col)] = (uint16_t)hb;
           }
         }
     }

@@ -215,5 +215,9 @@ NVFP4_HD int64_t c_offset(int32_t row0, int32_t row, int32_t ldc, int32_t n0, in
   return ((int64_t)row0 + row) * ldc + n0 + c4;
 }
 
+// Element offset of column `col` of row `p` in a row-major matrix with `ld`
+// columns (the GEMM1 debug dumps of C1 and h).
+NVFP4_HD int64_t row_major(int64_t p, int32_t ld, int32_t col) { return p * ld + col; }
+
 }  // namespace gemm_map
 }  // namespace nvfp4

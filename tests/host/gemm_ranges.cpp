@@ -125,12 +125,12 @@ void check_gemm(const Case& c, bool gemm1) {
         for (int row = 0; row < tl.rows; ++row)
           for (int ccol = 0; ccol < 32; ccol += 31) {
             const int32_t col = tl.nt * 32 * sh.waves + 32 * wave + ccol;
-            check_range("C1 gate dump", c_offset(tl.row0, row, 2 * I, col, 0),
-                        c_offset(tl.row0, row, 2 * I, col, 0) + 1, c1_elems);
-            check_range("C1 up dump", c_offset(tl.row0, row, 2 * I, I + col, 0),
-                        c_offset(tl.row0, row, 2 * I, I + col, 0) + 1, c1_elems);
-            check_range("h dump", c_offset(tl.row0, row, I, col, 0),
-                        c_offset(tl.row0, row, I, col, 0) + 1, h_elems);
+            const int64_t p = tl.row0 + row;
+            check_range("C1 gate dump", row_major(p, 2 * I, col), row_major(p, 2 * I, col) + 1,
+                        c1_elems);
+            check_range("C1 up dump", row_major(p, 2 * I, I + col),
+                        row_major(p, 2 * I, I + col) + 1, c1_elems);
+            check_range("h dump", row_major(p, I, col), row_major(p, I, col) + 1, h_elems);
           }
       } else {
         for (int row = 0; row < tl.rows; ++row)
