@@ -48,6 +48,8 @@ def parse_args():
                     help="skip the weight-only (W4A16) sub-measurement")
     ap.add_argument("--no-mx", action="store_true",
                     help="skip the UE8M0 (MX-style) sub-measurement")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the 30-layer stack sub-measurement of the prefill run")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--cpu-passes", type=int, default=2,
                     help="oracle layer forwards timed over the sample (about 7 s each at 4096 tokens)")
@@ -157,19 +159,40 @@ def build_layer(w, torch, M, layer=0, mx=False):
     return lay
 
 
+CLOCK_WARM_S = 0.5      # untimed GPU work before any timed pass
+
+
+def warm_clocks(torch, step, seconds=CLOCK_WARM_S):
+    """Run `step(i)` until `seconds` of wall time have passed, synchronising
+    every few steps.  After the GPU has been idle, its first ~20 prefill
+    steps (~13 ms) run 15% slower than the steady state (measured per step
+    with events on an MI355X: 650-660 us, then 568-580 us from step ~50 on),
+    which a handful of warm-up steps does not cover."""
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
+    return i
+
+
 def time_steps(torch, L, events, runs, steps, warmup, T, k, stage_events=True, fwd=None):
     """Time `steps` calls of nvfp4_moe_forward cycling over `runs` (list of
     (weights, workspace tensor, x, logits, out)); HIP events on torch's
     current stream, which the library launches on.  `fwd` replaces
     nvfp4_moe_forward (the weight-only forward has the same signature).
 
-    Two timed passes over the same steps: the first, uninstrumented, gives
-    the step time; the second records HIP events before the first launch
-    and after every kernel of every step and gives the per-kernel times.
-    (An event record costs about 3.5 µs of GPU time on this stack, so
-    instrumenting the first pass would add ~20 µs to every step.)  Returns
-    (ms per step, host wall s, per-stage µs or None, instrumented ms per
-    step or None)."""
+    After the `warmup` steps and CLOCK_WARM_S of untimed steps, two passes
+    over the same steps: the first records HIP events before the first launch
+    and after every kernel of every step and gives the per-kernel times; the
+    second, uninstrumented, gives the step time.  (An event record costs
+    about 3.5 us of GPU time on this stack, so instrumenting the pass that
+    gives the step time would add ~20 us to every step; running it second
+    means it starts from a GPU that has been busy for a while.)  Returns
+    (ms per step, host wall s, per-stage us or None, instrumented ms per step
+    or None)."""
     fwd = fwd or L.moe_forward
     stream = torch.cuda.current_stream().cuda_stream
     nst = len(L.MOE_STAGES)
@@ -194,19 +217,20 @@ def time_steps(torch, L, events, runs, steps, warmup, T, k, stage_events=True, f
 
     for i in range(warmup):
         step(i)
+    warm_clocks(torch, step)
+    stage_us = ms_instr = None
+    if stage_events:
+        evs = [events.create(nst + 1) for _ in range(steps)]
+        dbgs = [L.MoEDebug(stage_events=ctypes.cast(e, ctypes.POINTER(ctypes.c_void_p)))
+                for e in evs]
+        ms_instr, _ = timed(dbgs)
+        stage_ms = np.zeros(nst)
+        for e in evs:
+            for s_ in range(nst):
+                stage_ms[s_] += events.elapsed_ms(e[s_], e[s_ + 1])
+            events.destroy(e)
+        stage_us = {name: 1000.0 * v / steps for name, v in zip(L.MOE_STAGES, stage_ms)}
     ms_step, wall = timed(None)
-    if not stage_events:
-        return ms_step, wall, None, None
-    evs = [events.create(nst + 1) for _ in range(steps)]
-    dbgs = [L.MoEDebug(stage_events=ctypes.cast(e, ctypes.POINTER(ctypes.c_void_p)))
-            for e in evs]
-    ms_instr, _ = timed(dbgs)
-    stage_ms = np.zeros(nst)
-    for e in evs:
-        for s_ in range(nst):
-            stage_ms[s_] += events.elapsed_ms(e[s_], e[s_ + 1])
-        events.destroy(e)
-    stage_us = {name: 1000.0 * v / steps for name, v in zip(L.MOE_STAGES, stage_ms)}
     return ms_step, wall, stage_us, ms_instr
 
 
@@ -350,6 +374,7 @@ def bench_stack(args, torch, M, L, events):
 
     one_pass()
     torch.cuda.synchronize()
+    warm_clocks(torch, lambda i: one_pass() if i % 8 == 0 else None)
     passes = 3
     ev = events.create(2)
     events.record(ev[0], stream)
@@ -361,7 +386,10 @@ def bench_stack(args, torch, M, L, events):
     events.destroy(ev)
     flops = 6.0 * w.T * w.k * w.H * w.I * w.layers
     tflops = flops / (ms * 1e-3) / 1e12
-    return w, dict(ms_per_stack=round(ms, 3), tokens_per_s=round(w.T / (ms * 1e-3), 1),
+    return w, dict(workload=f"30-layer MoE stack: {w.T} tokens, hidden {w.H}, {w.E} experts, "
+                            f"intermediate {w.I}, top-{w.k}, Zipf(1.1) routing with empty "
+                            f"experts, residual add between layers",
+                   ms_per_stack=round(ms, 3), tokens_per_s=round(w.T / (ms * 1e-3), 1),
                    layer_tokens_per_s=round(w.T * w.layers / (ms * 1e-3), 1),
                    expert_gemm_flops=flops, tflops_whole_stack=round(tflops, 1),
                    frac_of_f16_peak=round(tflops / MFMA_F16_PEAK_TFLOPS, 4), passes=passes)
@@ -389,12 +417,15 @@ def copy_ceiling(torch, events):
 
 
 def bench_quantizer(args, torch, M, L, events):
-    """nvfp4_quantize_experts alone on the quantiser workload, 3 rotating
-    input/output sets (> last-level cache)."""
+    """The quantiser alone on the quantiser workload, 3 rotating input/output
+    sets (> last-level cache): nvfp4_quantize_pairs, the form the layer runs
+    (each token row read once for its 8 destination rows; the headline), and
+    the gather form nvfp4_quantize_experts over the permuted rows."""
     import synthetic as S
     w = S.WORKLOADS["quant"]
     xc, lc = S.calibration_batch(w)
-    # per-expert input scale from the calibration batch, with the library
+    # per-expert input scale from the calibration batch, with the library's
+    # calibration pass and load-time check
     dev = "cuda"
     Tc = xc.shape[0]
     ids = torch.empty((Tc, w.k), dtype=torch.int32, device=dev)
@@ -404,10 +435,11 @@ def bench_quantizer(args, torch, M, L, events):
     inv = torch.empty(Tc * w.k, dtype=torch.int32, device=dev)
     L.route_topk(torch.from_numpy(lc).cuda(), Tc, w.E, w.k, ids, wts)
     L.permute(ids, Tc, w.k, w.E, off, src, inv)
-    amax = torch.empty(w.E, dtype=torch.float32, device=dev)
-    L.expert_absmax(M.bf16_tensor(xc), w.H, w.H, src, w.k, off, w.E, Tc * w.k, amax)
-    s13 = (amax.cpu().numpy() / M.NVFP4_RANGE).astype(np.float32)
-    st, gs, _, _ = L.validate_scales(s13, (np.diff(off.cpu().numpy()) > 0).astype(np.uint8))
+    s13 = torch.empty(w.E, dtype=torch.float32, device=dev)
+    written = torch.empty(w.E, dtype=torch.uint8, device=dev)
+    L.calibrate_input_scales(M.bf16_tensor(xc), w.H, w.H, src, w.k, off, w.E, Tc * w.k, s13,
+                             written)
+    st, gs, _, _ = L.validate_scales(s13.cpu().numpy(), written.cpu().numpy())
     if st != L.OK:
         raise RuntimeError("quantiser workload calibration left unwritten slots")
     gs_d = torch.from_numpy(gs).cuda()
@@ -422,27 +454,37 @@ def bench_quantizer(args, torch, M, L, events):
         inv = torch.empty(w.P, dtype=torch.int32, device=dev)
         L.route_topk(lg, w.T, w.E, w.k, ids, wts)
         L.permute(ids, w.T, w.k, w.E, off, src, inv)
+        src_row = torch.div(src, w.k, rounding_mode="floor").to(torch.int32)
         codes = torch.empty((w.P, w.H // 2), dtype=torch.uint8, device=dev)
         sf = torch.empty((w.P, w.H // 16), dtype=torch.uint8, device=dev)
-        sets.append((x, ids, inv, codes, sf))
+        sets.append((x, ids, inv, off, src_row, codes, sf))
     stream = torch.cuda.current_stream().cuda_stream
 
-    def step(i):
-        x, ids, inv, codes, sf = sets[i % 3]
-        L.quantize_experts(x, w.H, w.T, w.H, w.k, ids, inv, w.E, gs_d, codes, sf, w.P, stream)
+    def pairs(i):
+        x, ids, inv, off, src_row, codes, sf = sets[i % 3]
+        L.quantize_pairs(x, w.H, w.T, w.H, w.k, ids, inv, w.E, gs_d, codes, sf, w.P, stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    n = max(args.steps, 50)
-    ev = events.create(2)
-    events.record(ev[0], stream)
-    for i in range(n):
-        step(i)
-    events.record(ev[1], stream)
-    torch.cuda.synchronize()
-    us = 1000.0 * events.elapsed_ms(ev[0], ev[1]) / n
-    events.destroy(ev)
+    def gather(i):
+        x, ids, inv, off, src_row, codes, sf = sets[i % 3]
+        L.quantize_experts(x, w.H, w.H, src_row, w.T, w.P, off, w.E, gs_d, codes, sf, stream)
+
+    def timed(step):
+        for i in range(args.warmup):
+            step(i)
+        warm_clocks(torch, step)
+        n = max(args.steps, 50)
+        ev = events.create(2)
+        events.record(ev[0], stream)
+        for i in range(n):
+            step(i)
+        events.record(ev[1], stream)
+        torch.cuda.synchronize()
+        us = 1000.0 * events.elapsed_ms(ev[0], ev[1]) / n
+        events.destroy(ev)
+        return us
+
+    us = timed(pairs)
+    us_gather = timed(gather)
     # algorithmic bytes: unique x once, routing ids + destinations, scales,
     # packed codes and E4M3 block scales written
     read = w.T * w.H * 2 + w.P * 4 * 2 + w.E * 4
@@ -450,20 +492,53 @@ def bench_quantizer(args, torch, M, L, events):
     gbps = (read + write) / (us * 1e-6) / 1e9
     return dict(workload="quantizer alone: 8192 tokens x hidden 2816 bf16, top-8 of 128 experts, "
                          "1% outlier channels x50",
+                kernel="quantize_experts_kernel (nvfp4_quantize_pairs, the layer's form)",
                 us_per_launch=round(us, 3), algorithmic_bytes=int(read + write),
-                gbps=round(gbps, 1), peak_gbps=HBM_PEAK_GBPS, frac=round(gbps / HBM_PEAK_GBPS, 4))
+                gbps=round(gbps, 1), peak_gbps=HBM_PEAK_GBPS, frac=round(gbps / HBM_PEAK_GBPS, 4),
+                gather_form_us=round(us_gather, 3),
+                gather_form_gbps=round((read + write) / (us_gather * 1e-6) / 1e9, 1))
+
+
+def blas_info():
+    """The BLAS library NumPy's fp64 GEMMs run on, and its thread count."""
+    try:
+        from threadpoolctl import threadpool_info
+        for d in threadpool_info():
+            if d.get("user_api") == "blas":
+                return dict(vendor=d.get("internal_api"), version=d.get("version"),
+                            threads=d.get("num_threads"))
+    except Exception:                                     # reported as unknown
+        pass
+    return dict(vendor=None, version=None, threads=None)
+
+
+def _timed_repeats(fn, min_seconds):
+    """Call fn() until min_seconds have passed (at least once); return
+    (calls, seconds)."""
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            return n, dt
 
 
 def cpu_baseline(args, w):
-    """The CPU oracle, unchanged, timed on a bounded sample of the workload:
-    its own NVFP4 layer (prepared untimed), then ``cpu_passes`` layer forwards
-    over the first ``cpu_sample_tokens`` tokens of the benchmark batch."""
+    """The CPU oracle, unchanged, timed on bounded samples: the headline is
+    the prefill layer (its own NVFP4 layer, prepared untimed, then
+    ``cpu_passes`` layer forwards over the first ``cpu_sample_tokens`` tokens
+    of the benchmark batch); beside it, the other workloads: the quantiser
+    alone on 512 tokens of its batch, the 16-token decode layer, and one layer
+    of the 30-layer stack on 512 tokens."""
     import synthetic as S
     from oracle import moe as OM
+    from oracle import quant as OQ
+    threads = min(16, os.cpu_count() or 1)
     t0 = time.time()
     w13, w2 = S.expert_weights(w)
     xc, lc = S.calibration_batch(w)
-    layer = OM.prepare_layer(w13, w2, xc, lc, w.k, threads=min(16, os.cpu_count() or 1))
+    layer = OM.prepare_layer(w13, w2, xc, lc, w.k, threads=threads)
     del w13, w2
     log(f"oracle layer prepared in {time.time() - t0:.1f}s (untimed)")
     n = args.cpu_sample_tokens
@@ -475,13 +550,60 @@ def cpu_baseline(args, w):
         OM.layer_forward(layer, x, lg, w.k)
     dt = time.perf_counter() - t0
     cores = len(os.sched_getaffinity(0))
+    blas = blas_info()
+    per = {}
+
+    # the 16-token decode layer (the same layer as the prefill one)
+    wd = S.WORKLOADS["decode"]
+    xd, ld = S.activations(wd), S.router_logits(wd)
+    reps, sec = _timed_repeats(lambda: OM.layer_forward(layer, xd, ld, wd.k), 2.0)
+    per["decode"] = dict(tokens_per_s=round(reps * wd.T / sec, 3), seconds=round(sec, 2),
+                         sample=f"{reps} full forwards of the {wd.T}-token decode batch")
+    del layer
+
+    # the quantiser alone (route, permute and scales untimed; the timed part
+    # is the per-expert quantisation of every routed row, as on the GPU)
+    wq = S.WORKLOADS["quant"]
+    nq = 512
+    s13, written = OM.calibrate_input_scale(*S.calibration_batch(wq), wq.k, wq.E)
+    ok, gs, _ = OM.validate_scales(s13, written)
+    xq = S.activations(wq, tokens=nq)
+    ids, _ = OM.route(S.router_logits(wq, tokens=nq), wq.k)
+    off, src, _ = OM.permute(ids, wq.E)
+    rexp = OM.row_experts(off)
+    xp = xq[src // wq.k]
+    reps, sec = _timed_repeats(lambda: OQ.quantize_experts(xp, rexp, gs), 2.0)
+    qbytes = nq * wq.H * 2 + nq * wq.k * 8 + wq.E * 4 + nq * wq.k * (wq.H // 2 + wq.H // 16)
+    per["quantizer"] = dict(tokens_per_s=round(reps * nq / sec, 3),
+                            gbps=round(reps * qbytes / sec / 1e9, 4), seconds=round(sec, 2),
+                            cores=1, sample=f"{reps} quantisations of the {nq * wq.k} routed "
+                                            f"rows of the first {nq} tokens (NumPy, one core)")
+
+    # one layer of the 30-layer stack
+    ws = S.WORKLOADS["stack"]
+    t0 = time.time()
+    w13, w2 = S.expert_weights(ws, layer=0)
+    xc, lc = S.calibration_batch(ws, layer=0)
+    slayer = OM.prepare_layer(w13, w2, xc, lc, ws.k, threads=threads)
+    del w13, w2
+    log(f"oracle stack layer prepared in {time.time() - t0:.1f}s (untimed)")
+    ns = 512
+    xs, ls = S.activations(ws, tokens=ns), S.router_logits(ws, layer=0, tokens=ns)
+    reps, sec = _timed_repeats(lambda: OM.layer_forward(slayer, xs, ls, ws.k, xs), 2.0)
+    per["stack_layer"] = dict(tokens_per_s=round(reps * ns / sec, 3),
+                              stack_tokens_per_s=round(reps * ns / sec / ws.layers, 3),
+                              seconds=round(sec, 2),
+                              sample=f"{reps} forwards of layer 0 of the stack on its first {ns} "
+                                     f"tokens (Zipf routing, residual)")
     return dict(value=round(passes * n / dt, 3), unit="tokens/s", cores=cores, kind="oracle",
-                seconds=round(dt, 2),
+                seconds=round(dt, 2), blas=blas,
                 sample=f"first {n} tokens of the {args.workload} batch, {passes} full layer "
                        f"forward(s) "
                        f"(route, permute, quantise, fp64 GEMMs over dequantised operands, "
                        f"SiLU*mul, requant, combine); NumPy elementwise work single-threaded, "
-                       f"fp64 GEMMs on the BLAS thread pool ({cores} cores visible)")
+                       f"fp64 GEMMs on {blas['vendor']} with {blas['threads']} threads "
+                       f"({cores} cores visible)",
+                per_workload=per)
 
 
 def main():
@@ -502,7 +624,7 @@ def main():
     events = HipEvents()
 
     import synthetic as S
-    decode = copy_gbps = quant = cpu = w4a16 = mx = ms_instr = None
+    decode = copy_gbps = quant = cpu = w4a16 = mx = ms_instr = stack = None
     if args.workload == "stack":
         w, st = bench_stack(args, torch, M, L, events)
         ms_step, wall, stage_us = st["ms_per_stack"], None, None
@@ -549,6 +671,9 @@ def main():
             if not args.no_mx:
                 mx = bench_mx(args, torch, M, L, events)
                 log(f"mx: {mx}")
+            if not args.no_stack:
+                _, stack = bench_stack(args, torch, M, L, events)
+                log(f"stack: {stack}")
         else:                                             # decode
             w = S.WORKLOADS["decode"]
             second = build_layer(w, torch, M, layer=1)
@@ -564,7 +689,7 @@ def main():
                             frac=decode["gemm1_frac_of_hbm_peak"], traffic=None,
                             experts_hit=decode["experts_hit"], us_per_launch=round(g1, 2))
             gemms = None
-        extra = dict(decode=decode, w4a16=w4a16, mx=mx)
+        extra = dict(decode=decode, w4a16=w4a16, mx=mx, stack=stack)
         del layer
 
     if args.workload == "prefill":

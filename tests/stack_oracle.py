@@ -17,11 +17,21 @@ FIELDS = ("w13c", "w13s", "w13s2", "w2c", "w2s", "w2s2", "w13_input_scale", "w2_
           "written13", "written2")
 
 
-def prepare_stack_layer(layer_idx: int, threads: int = 3) -> dict:
+def init_worker(threads: int) -> None:
+    """Cap the worker's BLAS and OpenMP pools at `threads`, so that several
+    workers share the host's cores instead of each starting one thread per
+    core."""
+    from threadpoolctl import threadpool_limits
+    globals()["_limits"] = threadpool_limits(limits=threads)
+    globals()["_threads"] = threads
+
+
+def prepare_stack_layer(layer_idx: int, threads: int = 0) -> dict:
     """The oracle's layer `layer_idx` of the stack workload (weights drawn,
     quantised and its activation scales calibrated by the oracle), as plain
     arrays."""
     t0 = time.perf_counter()
+    threads = threads or globals().get("_threads", 2)
     w = S.WORKLOADS["stack"]
     w13, w2 = S.expert_weights(w, layer=layer_idx, threads=threads)
     xc, lc = S.calibration_batch(w, layer=layer_idx)
