@@ -462,6 +462,10 @@ def bench_quantizer(args, torch, M, L, events):
 
     def pairs(i):
         x, ids, inv, off, src_row, codes, sf = sets[i % 3]
+        L.quantize_pairs(x, w.H, w.T, w.H, w.k, ids, None, w.E, gs_d, codes, sf, w.P, stream)
+
+    def pairs_grouped(i):
+        x, ids, inv, off, src_row, codes, sf = sets[i % 3]
         L.quantize_pairs(x, w.H, w.T, w.H, w.k, ids, inv, w.E, gs_d, codes, sf, w.P, stream)
 
     def gather(i):
@@ -484,19 +488,25 @@ def bench_quantizer(args, torch, M, L, events):
         return us
 
     us = timed(pairs)
+    us_grouped = timed(pairs_grouped)
     us_gather = timed(gather)
-    # algorithmic bytes: unique x once, routing ids + destinations, scales,
-    # packed codes and E4M3 block scales written
-    read = w.T * w.H * 2 + w.P * 4 * 2 + w.E * 4
+    # algorithmic bytes: unique x once, the routing ids, the scales, packed
+    # codes and E4M3 block scales written (the grouped forms also read one
+    # destination / source index per row)
+    read = w.T * w.H * 2 + w.P * 4 + w.E * 4
     write = w.P * (w.H // 2) + w.P * (w.H // 16)
-    gbps = (read + write) / (us * 1e-6) / 1e9
+    alg = read + write
+    gbps = alg / (us * 1e-6) / 1e9
     return dict(workload="quantizer alone: 8192 tokens x hidden 2816 bf16, top-8 of 128 experts, "
                          "1% outlier channels x50",
-                kernel="quantize_experts_kernel (nvfp4_quantize_pairs, the layer's form)",
-                us_per_launch=round(us, 3), algorithmic_bytes=int(read + write),
+                kernel="quantize_pairs_fast_kernel<false> (nvfp4_quantize_pairs, rows in "
+                       "(token, slot) order: the layer's form)",
+                us_per_launch=round(us, 3), algorithmic_bytes=int(alg),
                 gbps=round(gbps, 1), peak_gbps=HBM_PEAK_GBPS, frac=round(gbps / HBM_PEAK_GBPS, 4),
+                grouped_rows_us=round(us_grouped, 3),
+                grouped_rows_gbps=round((alg + w.P * 4) / (us_grouped * 1e-6) / 1e9, 1),
                 gather_form_us=round(us_gather, 3),
-                gather_form_gbps=round((read + write) / (us_gather * 1e-6) / 1e9, 1))
+                gather_form_gbps=round((alg + w.P * 4) / (us_gather * 1e-6) / 1e9, 1))
 
 
 def blas_info():

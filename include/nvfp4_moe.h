@@ -344,8 +344,8 @@ typedef struct {
   int32_t* expert_offsets;  /* [E+1]    */
   int32_t* src_pair;        /* [P]      */
   int32_t* inv_pair;        /* [P]      */
-  uint8_t* a1_codes;        /* [P, H/2] */
-  uint8_t* a1_sf;           /* [P, H/16]*/
+  uint8_t* a1_codes;        /* [P, H/2]  rows in (token, slot) order t*k + j */
+  uint8_t* a1_sf;           /* [P, H/16] the same order */
   float* c1;                /* [P, 2I]  fp32 w13 output incl. alpha1 */
   uint16_t* h;              /* [P, I]   bf16 SiLU(gate)*up           */
   uint8_t* a2_codes;        /* [P, I/2] */

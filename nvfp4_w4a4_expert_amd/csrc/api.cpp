@@ -392,8 +392,10 @@ nvfp4_status_t moe_forward(const nvfp4_moe_weights_t* w, const void* x_bf16,
   if (err == hipSuccess) err = mark(1);
   if (err == hipSuccess) err = launch_permute(ids, P, E, offsets, src_pair, inv, s);
   if (err == hipSuccess) err = mark(2);
+  // A1 rows are written in (token, slot) order q = t*k + j: each token's k
+  // rows are contiguous, and GEMM1 reads them through src_pair
   if (err == hipSuccess && !w16)
-    err = launch_quantize(static_cast<const uint16_t*>(x_bf16), H, T, H, k, ids, inv, E,
+    err = launch_quantize(static_cast<const uint16_t*>(x_bf16), H, T, H, k, ids, nullptr, E,
                           w->a1_gscale, a1c, a1s, P, s, false, mx);
   if (err == hipSuccess) err = mark(3);
   if (err == hipSuccess) {
@@ -404,6 +406,8 @@ nvfp4_status_t moe_forward(const nvfp4_moe_weights_t* w, const void* x_bf16,
     g1.c1_dbg = debug ? debug->c1 : nullptr;
     g1.h_dbg = debug && !w16 ? debug->h : nullptr;
     g1.mx = mx;
+    g1.a_src = src_pair;
+    g1.a_src_div = 1;
     if (w16) {
       g1.w16 = true;
       g1.a_rows = static_cast<const uint16_t*>(x_bf16);

@@ -153,7 +153,9 @@ __device__ __forceinline__ int32_t opaque_sgpr(int32_t v) {
 struct GemmParams {
   const uint8_t* a_codes;   // [P, K/2]
   const uint8_t* a_sf;      // [P, K/16]
-  // weight-only variant: A row p is a_rows[(a_src ? a_src[p] / a_src_div : p) * lda]
+  // A row of grouped row p: row a_src[p] / a_src_div of the operand (p when
+  // a_src is null) -- bf16 rows a_rows[.. * lda] (weight-only) or quantised
+  // rows of a_codes / a_sf
   const uint16_t* a_rows;   // bf16
   const int32_t* a_src;
   int64_t lda;
@@ -308,8 +310,11 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
       a_cp[i] = reinterpret_cast<const uint8_t*>(prm.a_rows + a_rows_offset(srow, prm.lda, kc, kCE));
       a_sp[i] = nullptr;
     } else {
-      a_cp[i] = prm.a_codes + a_codes_offset(arow, K, kc, kCE, kMX);
-      a_sp[i] = prm.a_sf + a_scales_offset(arow, K, kc, kCE, kMX);
+      // GEMM1 reads A1 through the permutation (its rows are stored in
+      // (token, slot) order); GEMM2's A2 rows are in grouped order
+      const int64_t qrow = prm.a_src ? prm.a_src[arow] / prm.a_src_div : arow;
+      a_cp[i] = prm.a_codes + a_codes_offset(qrow, K, kc, kCE, kMX);
+      a_sp[i] = prm.a_sf + a_scales_offset(qrow, K, kc, kCE, kMX);
     }
     a_lds[i] = kMX ? r * kLdAb + 16 * kc : r * kLdA + kCE * kc;
     a_lds_s[i] = kScOff + r * (kBK / 32) + kc;

@@ -119,11 +119,13 @@ __global__ __launch_bounds__(1024) void quantize_experts_kernel(
   }
 }
 
-// The layer's case of the kernel above (expert ids, destination rows and
-// scales all given, bf16 rows, E4M3 scales), specialised: the workgroup is
-// exactly one lane per block of the row (no idle lanes, so no per-lane
-// guards), destination offsets are 32-bit, and every scale word is whole.
-// Measured on the 8192 x 2816 top-8 workload: 33.5 -> 32.2 us.
+// The layer's case of the kernel above (expert ids and scales given, bf16
+// rows, E4M3 scales; destination rows given, or the identity when kP is
+// false), specialised: the workgroup is exactly one lane per block of the
+// row (no idle lanes, so no per-lane guards), destination offsets are 32-bit,
+// and every scale word is whole.  Measured on the 8192 x 2816 top-8 workload
+// with routed destinations: 33.5 -> 32.2 us.
+template <bool kP>
 __global__ __launch_bounds__(1024) void quantize_pairs_fast_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int32_t nblk, int32_t topk,
     const int32_t* __restrict__ expert_idx, const int32_t* __restrict__ dst_row,
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(1024) void quantize_pairs_fast_kernel(
     for (int jj = 0; jj < kBatch; ++jj) {
       const int64_t q = (int64_t)t * topk + min(j0 + jj, topk - 1);
       eb[jj] = expert_idx[q];
-      pb[jj] = dst_row[q];
+      pb[jj] = kP ? dst_row[q] : (int32_t)q;
     }
 #pragma unroll
     for (int jj = 0; jj < kBatch; ++jj) gb[jj] = gscale[min(max(eb[jj], 0), num_experts - 1)];
@@ -282,12 +284,17 @@ hipError_t launch_quantize(const uint16_t* x, int64_t ldx, int32_t num_rows, int
   if ((int64_t)num_rows * nblk == 0) return hipSuccess;
   // the layer's case: one workgroup of exactly nblk lanes per row, whole
   // scale words, 32-bit destination offsets
-  if (expert_idx && dst_row && gscale && !fp16_input && !mx && nblk <= 1024 && nblk % 4 == 0 &&
+  if (expert_idx && gscale && !fp16_input && !mx && nblk <= 1024 && nblk % 4 == 0 &&
       (reinterpret_cast<uintptr_t>(sf) & 3) == 0 &&
       (int64_t)num_dst_rows * nblk * 8 <= (int64_t)UINT32_MAX) {
-    hipLaunchKernelGGL(quantize_pairs_fast_kernel, dim3((uint32_t)num_rows), dim3(nblk), 0,
-                       stream, x, ldx, nblk, topk, expert_idx, dst_row, num_experts, gscale,
-                       codes, sf, num_dst_rows);
+    if (dst_row)
+      hipLaunchKernelGGL(quantize_pairs_fast_kernel<true>, dim3((uint32_t)num_rows), dim3(nblk),
+                         0, stream, x, ldx, nblk, topk, expert_idx, dst_row, num_experts, gscale,
+                         codes, sf, num_dst_rows);
+    else
+      hipLaunchKernelGGL(quantize_pairs_fast_kernel<false>, dim3((uint32_t)num_rows), dim3(nblk),
+                         0, stream, x, ldx, nblk, topk, expert_idx, dst_row, num_experts, gscale,
+                         codes, sf, num_dst_rows);
     return hipGetLastError();
   }
   // 64-lane wavefronts covering the row's blocks, at most 1024 threads per

@@ -247,8 +247,9 @@ def check_layer_parity(layer: OM.Layer, x_bits, logits, k, residual_bits=None, l
     assert np.array_equal(got["expert_offsets"], ref["offsets"]), label + " offsets"
     assert np.array_equal(got["src_pair"], ref["src_pair"]), label + " src_pair"
     assert np.array_equal(got["inv_pair"], ref["inv"]), label + " inv_pair"
-    assert np.array_equal(got["a1_codes"], ref["a1"][0]), label + " A1 codes"
-    assert np.array_equal(got["a1_sf"], ref["a1"][1]), label + " A1 scales"
+    # A1 rows are dumped in (token, slot) order q; the oracle's in grouped order
+    assert np.array_equal(got["a1_codes"][ref["src_pair"]], ref["a1"][0]), label + " A1 codes"
+    assert np.array_equal(got["a1_sf"][ref["src_pair"]], ref["a1"][1]), label + " A1 scales"
 
     rexp = OM.row_experts(ref["offsets"])
     c1 = rel_l2_rows(got["c1"], ref["c1"])
@@ -381,10 +382,15 @@ def gather_token_subset(dev, logits, k, E, tokens, label=""):
     sub_ids, _ = OM.route(np.asarray(logits)[tokens], k)
     _, sub_src, _ = OM.permute(sub_ids, E)
     qs = sub_src.astype(np.int64)
-    rows = inv[tokens[qs // k] * k + qs % k].astype(np.int64)
+    q = tokens[qs // k] * k + qs % k                   # the pairs, in the subset's order
+    rows = inv[q].astype(np.int64)                     # their grouped rows
     rows_d = torch.from_numpy(rows).to(dev["c1"].device)
+    q_d = torch.from_numpy(q).to(dev["c1"].device)
     got = {name: dev[name].index_select(0, rows_d).cpu().numpy()
-           for name in ("a1_codes", "a1_sf", "c1", "h", "a2_codes", "a2_sf", "c2")}
+           for name in ("c1", "h", "a2_codes", "a2_sf", "c2")}
+    # A1 rows are dumped in (token, slot) order
+    got.update({name: dev[name].index_select(0, q_d).cpu().numpy()
+                for name in ("a1_codes", "a1_sf")})
     got["h"] = got["h"].view(np.uint16)
     tok_d = torch.from_numpy(tokens).to(dev["c1"].device)
     got["out"] = dev["out"].view(torch.int16).index_select(0, tok_d).cpu().numpy().view(

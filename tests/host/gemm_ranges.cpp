@@ -158,12 +158,18 @@ void check_gemm(const Case& c, bool gemm1) {
         check_range("A bf16 rows", (a_row_count - 1) * (int64_t)K + lo,
                     (a_row_count - 1) * (int64_t)K + hi, a_row_count * (int64_t)K);
       } else {
-        const int64_t co = a_codes_offset(arow, K, kc, ce, mx);
-        check_range("A codes", co + a_codes_step(0, bk),
-                    co + a_codes_step(nk - 1, bk) + (mx ? 16 : ce / 2), a_codes_bytes);
-        const int64_t so = a_scales_offset(arow, K, kc, ce, mx);
-        check_range("A scales", so + a_scales_step(0, bk, mx),
-                    so + a_scales_step(nk - 1, bk, mx) + (mx ? 1 : ce / 16), a_sf_bytes);
+        // GEMM1 reads A1 row src_pair[arow] (a permutation of [0, P), so
+        // any row of it), GEMM2 reads A2 row arow
+        const int64_t rows_read[3] = {arow, 0, (int64_t)P - 1};
+        for (int ri = 0; ri < (gemm1 ? 3 : 1); ++ri) {
+          const int64_t qrow = rows_read[ri];
+          const int64_t co = a_codes_offset(qrow, K, kc, ce, mx);
+          check_range("A codes", co + a_codes_step(0, bk),
+                      co + a_codes_step(nk - 1, bk) + (mx ? 16 : ce / 2), a_codes_bytes);
+          const int64_t so = a_scales_offset(qrow, K, kc, ce, mx);
+          check_range("A scales", so + a_scales_step(0, bk, mx),
+                      so + a_scales_step(nk - 1, bk, mx) + (mx ? 1 : ce / 16), a_sf_bytes);
+        }
       }
     }
 
