@@ -13,6 +13,7 @@ activation-scale calibration); they stand in for an offline exporter.
 """
 from __future__ import annotations
 
+import operator
 from dataclasses import dataclass
 from typing import Optional
 
@@ -110,27 +111,78 @@ class NVFP4MoELayer:
     _debug_names = ("topk_ids", "topk_weights", "expert_offsets", "src_pair", "inv_pair",
                     "a1_codes", "a1_sf", "c1", "h", "a2_codes", "a2_sf", "c2")
 
-    def workspace(self, T: int, k: int) -> torch.Tensor:
+    def _torch_stream(self, stream):
+        """The torch stream a call runs on (torch's current stream when None;
+        an integer is a raw HIP stream handle on the layer's device)."""
+        if stream is None:
+            return torch.cuda.current_stream(self.w13.device)
+        if isinstance(stream, int):
+            return torch.cuda.ExternalStream(stream, device=self.w13.device)
+        return stream
+
+    def workspace(self, T: int, k: int, stream=None) -> torch.Tensor:
+        """The workspace for a call on `stream`.  Each stream has its own
+        buffer, allocated while that stream is current, so the caching
+        allocator orders its reuse after the work queued on that stream; calls
+        on different streams never share a buffer."""
         n = self._workspace_size(T, k, self.weights())
-        if self._ws is None or self._ws.numel() < n:
-            self._ws = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
-        return self._ws
+        s = self._torch_stream(stream)
+        if self._ws is None:
+            self._ws = {}
+        ws = self._ws.get(s.cuda_stream)
+        if ws is None or ws.numel() < n:
+            with torch.cuda.stream(s):
+                ws = torch.empty(max(n, 256), dtype=torch.uint8, device=self.w13.device)
+            self._ws[s.cuda_stream] = ws
+        return ws
+
+    def _check_call(self, x, logits, k, residual, out):
+        """Shapes, dtypes, layout and device of a forward's tensors: every
+        pointer the library receives must cover the rows it reads or writes."""
+        dev = self.w13.device
+
+        def need(ok, msg):
+            if not ok:
+                raise ValueError(msg)
+
+        def on_dev(t):
+            return isinstance(t, torch.Tensor) and t.device == dev and t.is_contiguous()
+
+        need(on_dev(x) and x.dtype == torch.bfloat16 and x.dim() == 2 and x.shape[1] == self.H,
+             f"x must be a contiguous bf16 [T, {self.H}] tensor on {dev}")
+        T = int(x.shape[0])
+        need(on_dev(logits) and logits.dtype == torch.float32 and
+             tuple(logits.shape) == (T, self.E),
+             f"logits must be a contiguous fp32 [{T}, {self.E}] tensor on {dev}")
+        try:
+            k = operator.index(k)
+        except TypeError:
+            k = None
+        need(k is not None and 1 <= k <= self.E, f"k must be an integer in [1, {self.E}]")
+        for name, t in (("residual", residual), ("out", out)):
+            if t is not None:
+                need(on_dev(t) and t.dtype == torch.bfloat16 and t.shape == x.shape,
+                     f"{name} must be a contiguous bf16 [{T}, {self.H}] tensor on {dev}")
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor, k: int,
                 residual: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                 debug: bool = False, stream=None):
         """x bf16 [T, H], logits fp32 [T, E] -> out bf16 [T, H] (and a dict of
-        intermediates when debug=True)."""
+        intermediates when debug=True).  Raises ValueError for tensors of the
+        wrong dtype, shape, layout or device.  The call is queued on `stream`
+        (torch's current stream when None) and returns without waiting."""
+        self._check_call(x, logits, k, residual, out)
+        k = operator.index(k)
         T = int(x.shape[0])
         if out is None:
             out = torch.empty_like(x)
-        ws = self.workspace(T, k)
+        ws = self.workspace(T, k, stream)
         w = self.weights()
         dbg = None
         bufs = None
         if debug:
             P, H, I, E = T * k, self.H, self.I, self.E
-            dev = self.device
+            dev = self.w13.device
             shapes = dict(
                 topk_ids=((T, k), torch.int32), topk_weights=((T, k), torch.float32),
                 expert_offsets=((E + 1,), torch.int32), src_pair=((P,), torch.int32),
@@ -138,8 +190,9 @@ class NVFP4MoELayer:
                 a1_sf=((P, H // self._sf_block), torch.uint8), c1=((P, 2 * I), torch.float32),
                 h=((P, I), torch.int16), a2_codes=((P, I // 2), torch.uint8),
                 a2_sf=((P, I // self._sf_block), torch.uint8), c2=((P, H), torch.float32))
-            bufs = {name: torch.empty(shapes[name][0], dtype=shapes[name][1], device=dev)
-                    for name in self._debug_names}
+            with torch.cuda.stream(self._torch_stream(stream)):
+                bufs = {name: torch.empty(shapes[name][0], dtype=shapes[name][1], device=dev)
+                        for name in self._debug_names}
             dbg = _lib.MoEDebug(**{name: t.data_ptr() for name, t in bufs.items()})
         self._forward(w, x, logits, T, k, residual, out, ws, ws.numel(), dbg, stream)
         return (out, bufs) if debug else out
