@@ -538,9 +538,9 @@ def cpu_baseline(args, w):
     """The CPU oracle, unchanged, timed on bounded samples: the headline is
     the prefill layer (its own NVFP4 layer, prepared untimed, then
     ``cpu_passes`` layer forwards over the first ``cpu_sample_tokens`` tokens
-    of the benchmark batch); beside it, the other workloads: the quantiser
-    alone on 512 tokens of its batch, the 16-token decode layer, and one layer
-    of the 30-layer stack on 512 tokens."""
+    of the benchmark batch); beside it, the other workloads: the 64-token tiny
+    layer, the quantiser alone on 512 tokens of its batch, the 16-token decode
+    layer, and one layer of the 30-layer stack on 512 tokens."""
     import synthetic as S
     from oracle import moe as OM
     from oracle import quant as OQ
@@ -562,6 +562,17 @@ def cpu_baseline(args, w):
     cores = len(os.sched_getaffinity(0))
     blas = blas_info()
     per = {}
+
+    # the tiny layer (64 tokens, 4 experts, hidden 256, top-2), prepared untimed
+    wt = S.WORKLOADS["tiny"]
+    w13t, w2t = S.expert_weights(wt)
+    tlayer = OM.prepare_layer(w13t, w2t, *S.calibration_batch(wt), wt.k, threads=threads)
+    xt, lt = S.activations(wt), S.router_logits(wt)
+    reps, sec = _timed_repeats(lambda: OM.layer_forward(tlayer, xt, lt, wt.k), 1.0)
+    per["tiny"] = dict(tokens_per_s=round(reps * wt.T / sec, 3), seconds=round(sec, 2),
+                       sample=f"{reps} full forwards of the {wt.T}-token tiny layer "
+                              f"({wt.E} experts, hidden {wt.H}, top-{wt.k})")
+    del tlayer, w13t, w2t
 
     # the 16-token decode layer (the same layer as the prefill one)
     wd = S.WORKLOADS["decode"]
