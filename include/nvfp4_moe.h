@@ -336,7 +336,10 @@ typedef struct {
  * array of NVFP4_MOE_STAGES+1 hipEvent_t (created by the caller) recorded on
  * the stream before the first launch and after each stage: route, permute,
  * quantise A1, grouped w13 GEMM (+SiLU*mul+requant), grouped w2 GEMM,
- * combine.  Buffer dumps are copied after the last event. */
+ * combine.  In the E4M3 forward, when H/16 lies in [64, 1024], routing and
+ * the A1 quantisation run as one kernel: it is timed as the route stage and
+ * the quantise stage is empty.  Buffer dumps are copied after the last
+ * event. */
 #define NVFP4_MOE_STAGES 6
 typedef struct {
   int32_t* topk_ids;        /* [T, k]   */

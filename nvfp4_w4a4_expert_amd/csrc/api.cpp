@@ -388,13 +388,23 @@ nvfp4_status_t moe_forward(const nvfp4_moe_weights_t* w, const void* x_bf16,
     return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
   };
   hipError_t err = mark(0);
-  if (err == hipSuccess) err = launch_route(router_logits, T, E, k, ids, wts, s);
+  // A1 rows are written in (token, slot) order q = t*k + j: each token's k
+  // rows are contiguous, and GEMM1 reads them through src_pair.  The E4M3
+  // mode routes and quantises in one kernel where the fused kernel covers
+  // the shape (timed as the route stage; the quantise stage is then empty).
+  bool fused = false;
+  if (err == hipSuccess && !w16 && !mx) {
+    const hipError_t ferr = launch_route_quantize(
+        router_logits, T, E, k, ids, wts, static_cast<const uint16_t*>(x_bf16), H,
+        w->a1_gscale, a1c, a1s, s);
+    if (ferr == hipSuccess) fused = true;
+    else if (ferr != hipErrorNotSupported) err = ferr;
+  }
+  if (err == hipSuccess && !fused) err = launch_route(router_logits, T, E, k, ids, wts, s);
   if (err == hipSuccess) err = mark(1);
   if (err == hipSuccess) err = launch_permute(ids, P, E, offsets, src_pair, inv, s);
   if (err == hipSuccess) err = mark(2);
-  // A1 rows are written in (token, slot) order q = t*k + j: each token's k
-  // rows are contiguous, and GEMM1 reads them through src_pair
-  if (err == hipSuccess && !w16)
+  if (err == hipSuccess && !w16 && !fused)
     err = launch_quantize(static_cast<const uint16_t*>(x_bf16), H, T, H, k, ids, nullptr, E,
                           w->a1_gscale, a1c, a1s, P, s, false, mx);
   if (err == hipSuccess) err = mark(3);

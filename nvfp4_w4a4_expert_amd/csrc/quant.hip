@@ -17,6 +17,7 @@
 // scale count is a multiple of 4 (byte stores otherwise).
 #include "internal.h"
 #include "nvfp4_device.h"
+#include "route_token.h"
 
 namespace nvfp4 {
 
@@ -123,22 +124,27 @@ __global__ __launch_bounds__(1024) void quantize_experts_kernel(
 // rows, E4M3 scales; destination rows given, or the identity when kP is
 // false), specialised: the workgroup is exactly one lane per block of the
 // row (no idle lanes, so no per-lane guards), destination offsets are 32-bit,
-// and every scale word is whole.  Slots go in batches of 8: the batch's codes
-// and scale words are all computed first and its stores then issued back to
-// back (measured on the 8192 x 2816 top-8 workload, destinations in
-// (token, slot) order: 30.5 -> 28.5 us; storing each slot as soon as it is
-// encoded leaves the stores spread between the encoding instructions).
-template <bool kP>
-__global__ __launch_bounds__(1024) void quantize_pairs_fast_kernel(
-    const uint16_t* __restrict__ x, int64_t ldx, int32_t nblk, int32_t topk,
-    const int32_t* __restrict__ expert_idx, const int32_t* __restrict__ dst_row,
-    int32_t num_experts, const float* __restrict__ gscale, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ sf, int32_t num_dst_rows) {
+// and every scale word is whole.
+//
+// Lane b quantises block b of `x_row` once per slot j < topk with the
+// SFScaleVal of expert tok_ids[j], writing destination row tok_dst[j] (kP)
+// or q0 + j; a slot whose expert or destination row is out of range is
+// skipped.  Slots go in batches of 8: the batch's codes and scale words are
+// all computed first and its stores then issued back to back (measured on
+// the 8192 x 2816 top-8 workload, destinations in (token, slot) order: 30.5
+// -> 28.5 us; storing each slot as soon as it is encoded leaves the stores
+// spread between the encoding instructions).  kTopk > 0 fixes the slot count
+// at compile time.
+template <bool kP, int kTopk>
+__device__ __forceinline__ void quantize_token_slots(
+    const uint16_t* __restrict__ x_row, int32_t nblk, int32_t b, int32_t topk_arg,
+    const int32_t* tok_ids, const int32_t* tok_dst, int32_t q0, int32_t num_experts,
+    const float* __restrict__ gscale, uint8_t* __restrict__ codes, uint8_t* __restrict__ sf,
+    int32_t num_dst_rows) {
 #pragma clang fp contract(off)
-  const int32_t t = (int32_t)blockIdx.x;
-  const int32_t b = (int32_t)threadIdx.x;            // < nblk, by the launch
+  const int32_t topk = kTopk > 0 ? kTopk : topk_arg;
   float xv[16];
-  const u32x4* src = reinterpret_cast<const u32x4*>(x + (int64_t)t * ldx + (int64_t)b * 16);
+  const u32x4* src = reinterpret_cast<const u32x4*>(x_row + (int64_t)b * 16);
   const u32x4 v0 = __builtin_nontemporal_load(src);
   const u32x4 v1 = __builtin_nontemporal_load(src + 1);
   unpack_bf16x8(v0, xv);
@@ -151,9 +157,9 @@ __global__ __launch_bounds__(1024) void quantize_pairs_fast_kernel(
     float gb[kBatch];
 #pragma unroll
     for (int jj = 0; jj < kBatch; ++jj) {
-      const int64_t q = (int64_t)t * topk + min(j0 + jj, topk - 1);
-      eb[jj] = expert_idx[q];
-      pb[jj] = kP ? dst_row[q] : (int32_t)q;
+      const int32_t j = min(j0 + jj, topk - 1);
+      eb[jj] = tok_ids[j];
+      pb[jj] = kP ? tok_dst[j] : q0 + j;
     }
 #pragma unroll
     for (int jj = 0; jj < kBatch; ++jj) gb[jj] = gscale[min(max(eb[jj], 0), num_experts - 1)];
@@ -188,6 +194,50 @@ __global__ __launch_bounds__(1024) void quantize_pairs_fast_kernel(
               sw[jj];
     }
   }
+}
+
+template <bool kP, int kTopk>
+__global__ __launch_bounds__(1024) void quantize_pairs_fast_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, int32_t nblk, int32_t topk,
+    const int32_t* __restrict__ expert_idx, const int32_t* __restrict__ dst_row,
+    int32_t num_experts, const float* __restrict__ gscale, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ sf, int32_t num_dst_rows) {
+  const int32_t t = (int32_t)blockIdx.x;
+  const int64_t q0 = (int64_t)t * (kTopk > 0 ? kTopk : topk);
+  quantize_token_slots<kP, kTopk>(x + (int64_t)t * ldx, nblk, (int32_t)threadIdx.x, topk,
+                                  expert_idx + q0, kP ? dst_row + q0 : nullptr, (int32_t)q0,
+                                  num_experts, gscale, codes, sf, num_dst_rows);
+}
+
+// Routing and the A1 quantisation of the layer in one launch: workgroup t
+// (exactly H/16 >= 64 lanes) routes token t with its first wavefront (the
+// router's own code, route_token) and writes the token's k ids and weights;
+// after a barrier every lane quantises its block of the row into rows
+// t*k + j with the SFScaleVals of the picked experts.  This saves the
+// router's launch.
+template <int EPL, int kTopk>
+__global__ __launch_bounds__(1024) void route_quantize_kernel(
+    const float* __restrict__ logits, int32_t E, int32_t k_arg, int32_t* __restrict__ ids,
+    float* __restrict__ weights, const uint16_t* __restrict__ x, int32_t nblk,
+    const float* __restrict__ gscale, uint8_t* __restrict__ codes, uint8_t* __restrict__ sf,
+    int32_t num_dst_rows) {
+  __shared__ int32_t s_ids[32];
+  const int32_t k = kTopk > 0 ? kTopk : k_arg;
+  const int32_t t = (int32_t)blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    int32_t id;
+    float w;
+    route_token<EPL>(logits + (int64_t)t * E, E, k, lane, id, w);
+    if (lane < k) {
+      ids[(int64_t)t * k + lane] = id;
+      weights[(int64_t)t * k + lane] = w;
+      s_ids[lane] = id;
+    }
+  }
+  __syncthreads();
+  quantize_token_slots<false, kTopk>(x + (int64_t)t * nblk * 16, nblk, (int32_t)threadIdx.x, k,
+                                     s_ids, nullptr, t * k, E, gscale, codes, sf, num_dst_rows);
 }
 
 // Gather form: one workgroup per destination row p (grid.x) and one 16-element
@@ -303,14 +353,21 @@ hipError_t launch_quantize(const uint16_t* x, int64_t ldx, int32_t num_rows, int
   if (expert_idx && gscale && !fp16_input && !mx && nblk <= 1024 && nblk % 4 == 0 &&
       (reinterpret_cast<uintptr_t>(sf) & 3) == 0 &&
       (int64_t)num_dst_rows * nblk * 8 <= (int64_t)UINT32_MAX) {
-    if (dst_row)
-      hipLaunchKernelGGL(quantize_pairs_fast_kernel<true>, dim3((uint32_t)num_rows), dim3(nblk),
-                         0, stream, x, ldx, nblk, topk, expert_idx, dst_row, num_experts, gscale,
-                         codes, sf, num_dst_rows);
-    else
-      hipLaunchKernelGGL(quantize_pairs_fast_kernel<false>, dim3((uint32_t)num_rows), dim3(nblk),
-                         0, stream, x, ldx, nblk, topk, expert_idx, dst_row, num_experts, gscale,
-                         codes, sf, num_dst_rows);
+    // top-8, the layer's case, has its own instantiation (measured 29.9 ->
+    // 28.8 us on the 8192 x 2816 workload with destinations in token-slot
+    // order)
+#define NVFP4_FAST(kp, kk)                                                                       \
+  hipLaunchKernelGGL((quantize_pairs_fast_kernel<kp, kk>), dim3((uint32_t)num_rows), dim3(nblk), \
+                     0, stream, x, ldx, nblk, topk, expert_idx, dst_row, num_experts, gscale,    \
+                     codes, sf, num_dst_rows)
+    if (dst_row) {
+      if (topk == 8) NVFP4_FAST(true, 8);
+      else NVFP4_FAST(true, 0);
+    } else {
+      if (topk == 8) NVFP4_FAST(false, 8);
+      else NVFP4_FAST(false, 0);
+    }
+#undef NVFP4_FAST
     return hipGetLastError();
   }
   // 64-lane wavefronts covering the row's blocks, at most 1024 threads per
@@ -539,6 +596,36 @@ hipError_t launch_conversions_selftest(unsigned long long* count, hipStream_t st
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(conversions_selftest_kernel, dim3(8192), dim3(256), 0, stream, count);
+  return hipGetLastError();
+}
+
+
+hipError_t launch_route_quantize(const float* logits, int32_t T, int32_t E, int32_t k,
+                                 int32_t* ids, float* weights, const uint16_t* x, int32_t H,
+                                 const float* gscale, uint8_t* codes, uint8_t* sf,
+                                 hipStream_t stream) {
+  const int32_t nblk = H / 16;
+  if (T < 1 || E < 1 || E > 1024 || k < 1 || k > 32 || k > E || H % 64 || nblk < 64 ||
+      nblk > 1024 || !gscale || (reinterpret_cast<uintptr_t>(sf) & 3) != 0 ||
+      (int64_t)T * k * nblk * 8 > (int64_t)UINT32_MAX)
+    return hipErrorNotSupported;
+  const int32_t P = T * k;
+#define NVFP4_RQ(epl, kk)                                                                        \
+  hipLaunchKernelGGL((route_quantize_kernel<epl, kk>), dim3((uint32_t)T), dim3(nblk), 0, stream,  \
+                     logits, E, k, ids, weights, x, nblk, gscale, codes, sf, P)
+#define NVFP4_RQ_E(kk)                                                                           \
+  if (E <= 64) NVFP4_RQ(1, kk);                                                                  \
+  else if (E <= 128) NVFP4_RQ(2, kk);                                                            \
+  else if (E <= 256) NVFP4_RQ(4, kk);                                                            \
+  else if (E <= 512) NVFP4_RQ(8, kk);                                                            \
+  else NVFP4_RQ(16, kk);
+  if (k == 8) {
+    NVFP4_RQ_E(8)
+  } else {
+    NVFP4_RQ_E(0)
+  }
+#undef NVFP4_RQ_E
+#undef NVFP4_RQ
   return hipGetLastError();
 }
 

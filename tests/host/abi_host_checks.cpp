@@ -45,6 +45,16 @@ hipError_t launch_route(const float*, int32_t, int32_t, int32_t, int32_t*, float
   g_calls.push_back("route");
   return hipSuccess;
 }
+hipError_t launch_route_quantize(const float*, int32_t T, int32_t E, int32_t k, int32_t*,
+                                 float*, const uint16_t*, int32_t H, const float* gscale,
+                                 uint8_t* codes, uint8_t* sf, hipStream_t) {
+  // the shapes the real launcher covers; otherwise nothing is launched
+  if (T < 1 || E > 1024 || k > 32 || H % 64 || H / 16 < 64 || H / 16 > 1024)
+    return hipErrorNotSupported;
+  if (!gscale || !codes || !sf) abort();
+  g_calls.push_back("route_quantize");
+  return hipSuccess;
+}
 hipError_t launch_permute(const int32_t*, int32_t, int32_t, int32_t*, int32_t*, int32_t*,
                           hipStream_t) {
   g_calls.push_back("permute");
@@ -226,6 +236,48 @@ static void forward_checks() {
   CHECK(nvfp4_moe_forward_mx(&w, x, logits, T, k, nullptr, out, ws, ws_bytes, nullptr, nullptr) ==
         NVFP4_OK);
   CHECK(g_calls == nv && g_quant_mx == 1 && g_gemm1_mode == 2 && g_gemm2_mode == 2);
+
+  // hidden 1024 (H/16 = 64): routing and the A1 quantisation in one kernel,
+  // timed as the route stage; the weight-only and UE8M0 modes keep the
+  // separate router
+  {
+    nvfp4_moe_weights_t wf = w;
+    const int32_t Hf = 1024;
+    wf.hidden = Hf;
+    wf.w13 = (const uint8_t*)b.get((size_t)E * 2 * I * Hf / 2);
+    wf.w13_sf = (const uint8_t*)b.get((size_t)E * 2 * I * Hf / 16);
+    wf.w2 = (const uint8_t*)b.get((size_t)E * Hf * I / 2);
+    wf.w2_sf = (const uint8_t*)b.get((size_t)E * Hf * I / 16);
+    size_t wsf = 0, wsf16 = 0;
+    CHECK(nvfp4_moe_workspace_size(T, k, &wf, &wsf) == NVFP4_OK);
+    CHECK(nvfp4_moe_workspace_size_w4a16(T, k, &wf, &wsf16) == NVFP4_OK);
+    void* wsb = b.get(wsf > wsf16 ? wsf : wsf16);
+    void* xf = b.get((size_t)T * Hf * 2);
+    void* of = b.get((size_t)T * Hf * 2);
+    g_calls.clear();
+    CHECK(nvfp4_moe_forward(&wf, xf, logits, T, k, nullptr, of, wsb, wsf, nullptr, nullptr) ==
+          NVFP4_OK);
+    const std::vector<std::string> nvq = {"route_quantize", "permute", "gemm1", "gemm2",
+                                          "combine"};
+    CHECK(g_calls == nvq);
+    g_calls.clear();
+    CHECK(nvfp4_moe_forward(&wf, xf, logits, T, k, nullptr, of, wsb, wsf, &dbg, nullptr) ==
+          NVFP4_OK);
+    const std::vector<std::string> nvqd = {"event", "route_quantize", "event", "permute",
+                                           "event", "event", "gemm1", "event", "gemm2",
+                                           "event", "combine", "event", "copy"};
+    CHECK(g_calls == nvqd);
+    g_calls.clear();
+    CHECK(nvfp4_moe_forward_mx(&wf, xf, logits, T, k, nullptr, of, wsb, wsf, nullptr,
+                               nullptr) == NVFP4_OK);
+    CHECK(g_calls == nv && g_quant_mx == 1);
+    nvfp4_moe_weights_t wf16 = wf;
+    wf16.w13_input_scale = wf16.w2_input_scale = wf16.a1_gscale = wf16.a2_gscale = nullptr;
+    g_calls.clear();
+    CHECK(nvfp4_moe_forward_w4a16(&wf16, xf, logits, T, k, nullptr, of, wsb, wsf16, nullptr,
+                                  nullptr) == NVFP4_OK);
+    CHECK(g_calls == w16c);
+  }
 
   // argument checks: nothing is launched
   g_calls.clear();
