@@ -57,6 +57,12 @@ def _cases():
                                 ("maxsize", 0, None), ("shapes", 0, None)):
         w, T, counts = _workload_counts(name, layer, tokens)
         add(f"{name}-L{layer}-T{T}", w.E, w.H, w.I, w.k, T, counts)
+    # the fused routing + quantisation parity shapes (hidden 1024, I 64)
+    for E, k, T in ((64, 1, 5), (256, 32, 9), (512, 4, 33), (1024, 8, 3)):
+        w = S.Workload(f"fused-E{E}-k{k}", 8, T=T, H=1024, E=E, I=64, k=k, router="normal",
+                       calib_tokens=2048)
+        ids, _ = OM.route(S.router_logits(w), k)
+        add(w.name, E, 1024, 64, k, T, np.bincount(ids.reshape(-1), minlength=E))
     t = S.WORKLOADS["tiny"]
     for label, counts in TILE_COUNTS.items():
         add(f"tiles-{label}", t.E, t.H, t.I, 1, sum(counts), counts)

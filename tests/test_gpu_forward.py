@@ -136,6 +136,22 @@ def test_ring_tails_and_skewed_router():
     _report("shapes", m)
 
 
+@pytest.mark.parametrize("E,k,T", [(64, 1, 5), (256, 32, 9), (512, 4, 33), (1024, 8, 3)])
+def test_fused_routing_and_quantisation(E, k, T):
+    """hidden 1024 (H/16 = 64 lanes, the narrowest row the fused routing + A1
+    quantisation launch takes), with expert counts that select each router
+    width (64 to 1024 experts) and top-k other than 8 (the generic slot
+    loop) as well as 8: ids, weights, permutation and A1 exactly, the rest
+    within the bounds."""
+    w = S.Workload(f"fused-E{E}-k{k}", 8, T=T, H=1024, E=E, I=64, k=k, router="normal",
+                   calib_tokens=2048)
+    w13, w2 = S.expert_weights(w)
+    layer = OM.prepare_layer(w13, w2, *S.calibration_batch(w), k, threads=16)
+    del w13, w2
+    m = check_layer_parity(layer, S.activations(w), S.router_logits(w), k, label=w.name)
+    _report(w.name, m)
+
+
 def test_all_rows_on_two_experts():
     """Every token routed to experts 0 and 1: many m-tiles of one expert, six
     experts without rows."""
