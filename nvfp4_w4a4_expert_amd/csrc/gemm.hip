@@ -320,6 +320,13 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
     a_lds_s[i] = kScOff + r * (kBK / 32) + kc;
   }
 
+  // The tile's output scale.  The E4M3 w13 kernel loads it before the K loop,
+  // so that its wait is absorbed there instead of draining every outstanding
+  // load before the epilogue (w13 -1.3 us at the prefill layer); the other
+  // kernels load it after the loop, where the extra live register would spill.
+  constexpr bool kEarlyAlpha = kGated && kMode == kModeNV;
+  float alpha_early = 0.0f;
+  if constexpr (kEarlyAlpha) alpha_early = prm.in_scale[e] * prm.w_scale2[e];
   f32x16_t acc[kMBa][2];
 #pragma unroll
   for (int i = 0; i < kMBa; ++i)
@@ -573,7 +580,8 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
     if (nkr + i < nk) step(nkr + i, ic);
   });
 
-  const float alpha = kW16 ? prm.w_scale2[e] : prm.in_scale[e] * prm.w_scale2[e];
+  const float alpha = kEarlyAlpha ? alpha_early
+                     : kW16 ? prm.w_scale2[e] : prm.in_scale[e] * prm.w_scale2[e];
   // MFMA 32x32 output layout: lane holds column (lane & 31) and rows
   // 8 * (i / 4) + 4 * (lane / 32) + (i % 4) for accumulator element i.
   const int ccol = lane & 31, crow = 4 * g;
@@ -645,7 +653,7 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
           // silu(g) = g / (1 + e^-g); the hardware reciprocal (1 ulp) is far
           // inside the bf16 rounding that follows
           const float hv = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-          const uint32_t hb = f32_to_bf16(hv);
+          const uint32_t hb = __builtin_bit_cast(uint16_t, (__bf16)hv);   // RNE, hardware
           sh[row * kLdh + col] = (uint16_t)hb;
           if (row < rows) {
             const int64_t p = row0 + row;
