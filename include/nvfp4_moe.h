@@ -382,6 +382,11 @@ NVFP4_API nvfp4_status_t nvfp4_moe_workspace_size(int32_t num_tokens, int32_t k,
  * T*k <= 2^30, and (ceil(T*k/32) + min(T*k, E)) * max(ceil(I/128), ceil(H/256))
  * <= 2^31 - 1 (the GEMM tile count); else NVFP4_ERR_UNSUPPORTED.
  * T == 0 is a no-op.  Experts that receive no rows cost nothing.
+ * The call only enqueues kernels: it allocates nothing, clears nothing with
+ * memset and never synchronises the host.  With debug == NULL it may be
+ * captured into a HIP graph and replayed; a replay reads whatever the input
+ * buffers hold when it runs.  (Tested with one call on the device made
+ * before the capture, which does the one-time occupancy lookup.)
  */
 NVFP4_API nvfp4_status_t nvfp4_moe_forward(const nvfp4_moe_weights_t* w, const void* x_bf16,
                                            const float* router_logits, int32_t num_tokens,
