@@ -9,6 +9,7 @@
 
 #define NVFP4_BUILDING_LIBRARY 1
 #include "../../include/nvfp4_moe.h"
+#include "gemm_tiles.h"
 #include "internal.h"
 
 namespace {
@@ -402,7 +403,10 @@ nvfp4_status_t moe_forward(const nvfp4_moe_weights_t* w, const void* x_bf16,
   }
   if (err == hipSuccess && !fused) err = launch_route(router_logits, T, E, k, ids, wts, s);
   if (err == hipSuccess) err = mark(1);
-  if (err == hipSuccess) err = launch_permute(ids, P, E, offsets, src_pair, inv, s);
+  // Small batches: GEMM1 regroups the routed ids itself and writes offsets,
+  // src_pair and inv (the permute stage is then empty).
+  const bool fold = gemm_map::fold_permutation(P, E);
+  if (err == hipSuccess && !fold) err = launch_permute(ids, P, E, offsets, src_pair, inv, s);
   if (err == hipSuccess) err = mark(2);
   if (err == hipSuccess && !w16 && !fused)
     err = launch_quantize(static_cast<const uint16_t*>(x_bf16), H, T, H, k, ids, nullptr, E,
@@ -418,6 +422,10 @@ nvfp4_status_t moe_forward(const nvfp4_moe_weights_t* w, const void* x_bf16,
     g1.mx = mx;
     g1.a_src = src_pair;
     g1.a_src_div = 1;
+    if (fold) {
+      g1.perm_ids = ids;
+      g1.perm_offsets = offsets; g1.perm_src = src_pair; g1.perm_inv = inv;
+    }
     if (w16) {
       g1.w16 = true;
       g1.a_rows = static_cast<const uint16_t*>(x_bf16);

@@ -177,6 +177,14 @@ struct GemmParams {
   uint8_t* out_sf;          // [P, I/16]
   float* c1_dbg;            // [P, 2I] or null
   uint16_t* h_dbg;          // [P, I] or null
+  // small-batch GEMM1 only (gemm_map::fold_permutation): the routed expert
+  // ids of the P pairs; when set, the kernel derives the grouping from them
+  // instead of reading offsets / a_src, and writes the permutation out
+  const int32_t* perm_ids;  // [P] or null
+  int32_t perm_P;
+  int32_t* perm_offsets;    // [E+1], written by workgroup 0
+  int32_t* perm_src;        // [P] src_pair
+  int32_t* perm_inv;        // [P] inv
 };
 
 }  // namespace
@@ -202,43 +210,88 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
   __shared__ int32_t s_off[kMaxExperts + 1];             // expert row offsets
   __shared__ int32_t s_mt[kMaxExperts + 1];              // m-tiles before each expert
   __shared__ int32_t s_scan[kWaves];
+  // Small-batch GEMM1 regrouping the routed ids itself (prm.perm_ids set):
+  // the ids, a second scan's wave totals, and the pair of each row of the
+  // current tile.
+  constexpr bool kFold = kGated && kMB == 1;
+  __shared__ int32_t s_fids[kFold ? kFoldMaxPairs : 1];
+  __shared__ int32_t s_fscan[kFold ? kWaves : 1];
+  __shared__ int32_t s_fsrc[kFold ? 32 : 1];
+  const bool fold = kFold && prm.perm_ids != nullptr;
 
   // ---- once per workgroup: per-expert m-tile prefix in LDS -----------------
   {
     // entries 0 .. E of the prefix (E + 1 <= kMaxExperts + 1 of them)
     constexpr int kPer = (kMaxExperts + 1 + kThreads - 1) / kThreads;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int32_t cnt[kPer], total = 0;
+    if constexpr (kFold) {
+      if (fold) {
+        // histogram of the routed ids (pairs with an id outside [0, E) are
+        // left out, as the permutation kernel does); s_mt holds the counts
+        // until every thread has read its entries below
+        for (int e = tid; e < prm.E; e += kThreads) s_mt[e] = 0;
+        lds_barrier();
+        for (int32_t q = tid; q < prm.perm_P; q += kThreads) {
+          const int32_t id = prm.perm_ids[q];
+          s_fids[q] = id;
+          if ((uint32_t)id < (uint32_t)prm.E) atomicAdd(&s_mt[id], 1);
+        }
+        lds_barrier();
+      }
+    }
+    int32_t cnt[kPer], rcnt[kPer], total = 0, rtotal = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int32_t e = kPer * tid + i;
       int32_t m = 0;
       if (e < prm.E) {
-        const int32_t o0 = prm.offsets[e], o1 = prm.offsets[e + 1];
-        s_off[e] = o0;
-        if (e == prm.E - 1) s_off[prm.E] = o1;
-        m = o1 - o0;
+        if (fold) {
+          m = s_mt[e];
+        } else {
+          const int32_t o0 = prm.offsets[e], o1 = prm.offsets[e + 1];
+          s_off[e] = o0;
+          if (e == prm.E - 1) s_off[prm.E] = o1;
+          m = o1 - o0;
+        }
       }
       cnt[i] = (m + kBM - 1) / kBM;
+      rcnt[i] = m;
       total += cnt[i];
+      rtotal += m;
     }
-    int32_t incl = total;
+    int32_t incl = total, rincl = rtotal;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int32_t o = __shfl_up(incl, off, 64);
       if (lane >= off) incl += o;
+      if constexpr (kFold) {
+        const int32_t ro = __shfl_up(rincl, off, 64);
+        if (lane >= off) rincl += ro;
+      }
     }
-    if (lane == 63) s_scan[wave] = incl;
+    if (lane == 63) {
+      s_scan[wave] = incl;
+      if constexpr (kFold) s_fscan[wave] = rincl;
+    }
     lds_barrier();
-    int32_t base = incl - total;
-    for (int w = 0; w < wave; ++w) base += s_scan[w];
+    int32_t base = incl - total, rbase = rincl - rtotal;
+    for (int w = 0; w < wave; ++w) {
+      base += s_scan[w];
+      if constexpr (kFold) rbase += s_fscan[w];
+    }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int32_t e = kPer * tid + i;
-      if (e <= prm.E) s_mt[e] = base;
+      if (e <= prm.E) {
+        s_mt[e] = base;
+        if (fold) s_off[e] = rbase;     // expert offsets: exclusive prefix of the counts
+      }
       base += cnt[i];
+      rbase += rcnt[i];
     }
     lds_barrier();
+    if (fold && blockIdx.x == 0)
+      for (int e = tid; e <= prm.E; e += kThreads) prm.perm_offsets[e] = s_off[e];
   }
   const int32_t total_m = s_mt[prm.E];
   const int32_t total = total_m * prm.n_tiles;
@@ -256,6 +309,43 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
   const Tile tl = tile_of(logical, prm.n_tiles, s_mt, s_off, prm.E, kBM);
   const int32_t nt = tl.nt, e = tl.e, row0 = tl.row0, rows = tl.rows;
   if (rows <= 0) continue;                             // (uniform; never for consistent offsets)
+
+  // Regrouping from the routed ids: the tile's rows are ranks
+  // [row0 - offsets[e], + rows) among expert e's pairs in pair order (the
+  // stable order of the permutation).  Wavefront 0 walks the ids 64 at a
+  // time; a pair of expert e gets rank = matches before it, counted with a
+  // ballot.  The tile with n-tile 0 writes its rows of src_pair and inv.
+  if constexpr (kFold) {
+    if (fold) {
+      if (wave == 0) {
+        const int32_t lo = row0 - s_off[e];
+        const uint64_t below = (1ull << lane) - 1ull;
+        int32_t seen = 0;
+        for (int32_t c0 = 0; c0 < prm.perm_P; c0 += 64) {
+          const int32_t q = c0 + lane;
+          const bool match = q < prm.perm_P && s_fids[q] == e;
+          const uint64_t mask = __ballot(match);
+          if (match) {
+            const int32_t r = seen + __popcll(mask & below) - lo;
+            if (r >= 0 && r < rows) s_fsrc[r] = q;
+          }
+          seen += __popcll(mask);
+        }
+      }
+      lds_barrier();
+      if (nt == 0 && tid < rows) {
+        const int32_t q = s_fsrc[tid];
+        prm.perm_src[row0 + tid] = q;
+        prm.perm_inv[q] = row0 + tid;
+      }
+    }
+  }
+  // pair index of tile row arow (row0 <= arow < row0 + rows)
+  auto src_of = [&](int64_t arow) -> int32_t {
+    if constexpr (kFold)
+      if (fold) return s_fsrc[arow - row0];
+    return prm.a_src[arow];
+  };
 
   // ---- B streaming assignment: wave's 64 weight rows, 2 blocks of 32 ------
   // GEMM1: block 0 = gate rows, block 1 = the matching up rows.  Weights are
@@ -306,13 +396,13 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
     const int r = cc / kCPR, kc = cc % kCPR;
     const int64_t arow = a_row(row0, r, rows);
     if constexpr (kW16) {
-      const int64_t srow = prm.a_src ? prm.a_src[arow] / prm.a_src_div : arow;
+      const int64_t srow = prm.a_src ? src_of(arow) / prm.a_src_div : arow;
       a_cp[i] = reinterpret_cast<const uint8_t*>(prm.a_rows + a_rows_offset(srow, prm.lda, kc, kCE));
       a_sp[i] = nullptr;
     } else {
       // GEMM1 reads A1 through the permutation (its rows are stored in
       // (token, slot) order); GEMM2's A2 rows are in grouped order
-      const int64_t qrow = prm.a_src ? prm.a_src[arow] / prm.a_src_div : arow;
+      const int64_t qrow = prm.a_src ? src_of(arow) / prm.a_src_div : arow;
       a_cp[i] = prm.a_codes + a_codes_offset(qrow, K, kc, kCE, kMX);
       a_sp[i] = prm.a_sf + a_scales_offset(qrow, K, kc, kCE, kMX);
     }
@@ -813,6 +903,14 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream) {
   prm.E = a.E; prm.K = a.H; prm.N_w = 2 * a.I; prm.I = a.I;
   prm.out_gscale = a.out_gscale; prm.out_codes = a.out_codes; prm.out_sf = a.out_sf;
   prm.c1_dbg = a.c1_dbg; prm.h_dbg = a.h_dbg;
+  if (a.perm_ids) {
+    // only the small-batch kernels regroup the ids themselves, and only up
+    // to kFoldMaxPairs pairs (their LDS copy of the ids)
+    if (!fold_permutation(a.P, a.E) || !a.perm_offsets || !a.perm_src || !a.perm_inv || !a.a_src)
+      return hipErrorInvalidValue;
+    prm.perm_ids = a.perm_ids; prm.perm_P = a.P;
+    prm.perm_offsets = a.perm_offsets; prm.perm_src = a.perm_src; prm.perm_inv = a.perm_inv;
+  }
   const int mode = a.mx ? kModeMX : a.w16 ? kModeW16 : kModeNV;
   prm.n_tiles = n_tiles(true, select_shape(true, mode, a.P, a.E).waves, a.I, a.H);
   if (large_batch(a.P, a.E)) {

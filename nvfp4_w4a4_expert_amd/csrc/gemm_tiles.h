@@ -70,6 +70,16 @@ constexpr Shape kG2Small{4, 1, 64, 3, 2, false};
 // The large-batch kernels run when experts average at least 32 rows.
 NVFP4_HD bool large_batch(int32_t P, int32_t E) { return P >= 32 * E; }
 
+// Small batches of at most kFoldMaxPairs (token, slot) pairs skip the
+// permutation kernel: the small-batch GEMM1 regroups the routed ids itself
+// (every workgroup histograms them in LDS for the expert offsets and ranks
+// its own tile's pairs) and writes offsets, src_pair and inv for GEMM2, the
+// combine and the debug dumps.
+constexpr int kFoldMaxPairs = 512;
+NVFP4_HD bool fold_permutation(int32_t P, int32_t E) {
+  return !large_batch(P, E) && P <= kFoldMaxPairs;
+}
+
 NVFP4_HD Shape select_shape(bool gemm1, int mode, int32_t P, int32_t E) {
   if (large_batch(P, E)) {
     if (gemm1) return mode == kModeMX ? kG1LargeMx : mode == kModeW16 ? kG1LargeW16 : kG1Large;

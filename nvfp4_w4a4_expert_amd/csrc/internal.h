@@ -69,6 +69,14 @@ struct Gemm1Args {
   uint8_t* out_sf;          // [P, I/16]
   float* c1_dbg;            // [P, 2I] or null
   uint16_t* h_dbg;          // [P, I] or null
+  // When set (only if gemm_map::fold_permutation(P, E)), GEMM1 regroups the
+  // routed ids [P] itself instead of reading offsets / a_src, and writes the
+  // permutation (offsets [E+1], src_pair [P], inv [P]) for the later stages;
+  // a_src must still be non-null (it selects the gathered-row path).
+  const int32_t* perm_ids = nullptr;
+  int32_t* perm_offsets = nullptr;
+  int32_t* perm_src = nullptr;
+  int32_t* perm_inv = nullptr;
   int32_t P, E, H, I;
 };
 

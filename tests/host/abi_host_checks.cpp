@@ -22,6 +22,8 @@
 static std::vector<std::string> g_calls;
 static int g_quant_mx = -1, g_gemm1_mode = -1, g_gemm2_mode = -1;
 static int32_t g_gemm1_P = -1, g_quant_dst_rows = -1;
+// GEMM1 asked to regroup the routed ids itself (the permute kernel skipped)
+static bool g_gemm1_fold = false;
 static int g_gather_src_div = -1;
 
 namespace nvfp4 {
@@ -78,6 +80,8 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t) {
   g_calls.push_back("gemm1");
   g_gemm1_mode = a.mx ? 2 : a.w16 ? 1 : 0;
   g_gemm1_P = a.P;
+  g_gemm1_fold = a.perm_ids != nullptr;
+  if (g_gemm1_fold && !(a.perm_offsets && a.perm_src && a.perm_inv && a.a_src)) abort();
   return hipSuccess;
 }
 hipError_t launch_pack_weights(int32_t, const uint8_t*, const uint8_t*, int32_t, int32_t, int32_t,
@@ -191,13 +195,15 @@ static void forward_checks() {
   CHECK(nvfp4_moe_workspace_size_w4a16(T, k, &w, &ws16) == NVFP4_OK && ws16 > 0);
   void* ws = b.get(ws_bytes > ws16 ? ws_bytes : ws16);
 
-  // the E4M3 forward: stages in order, the quantiser writing T*k rows
+  // the E4M3 forward: stages in order, the quantiser writing T*k rows; 15
+  // pairs on 8 experts run the small-batch GEMMs, so GEMM1 regroups the
+  // routed ids itself and the permute kernel is not launched
   g_calls.clear();
   CHECK(nvfp4_moe_forward(&w, x, logits, T, k, nullptr, out, ws, ws_bytes, nullptr, nullptr) ==
         NVFP4_OK);
-  const std::vector<std::string> nv = {"route", "permute", "quantize", "gemm1", "gemm2", "combine"};
+  const std::vector<std::string> nv = {"route", "quantize", "gemm1", "gemm2", "combine"};
   CHECK(g_calls == nv);
-  CHECK(g_quant_mx == 0 && g_quant_dst_rows == T * k && g_gemm1_P == T * k);
+  CHECK(g_quant_mx == 0 && g_quant_dst_rows == T * k && g_gemm1_P == T * k && g_gemm1_fold);
   CHECK(g_gemm1_mode == 0 && g_gemm2_mode == 0);
   // one byte short of the workspace, or misaligned
   g_calls.clear();
@@ -215,7 +221,7 @@ static void forward_checks() {
   g_calls.clear();
   CHECK(nvfp4_moe_forward(&w, x, logits, T, k, nullptr, out, ws, ws_bytes, &dbg, nullptr) ==
         NVFP4_OK);
-  const std::vector<std::string> nvd = {"event", "route", "event", "permute", "event", "quantize",
+  const std::vector<std::string> nvd = {"event", "route", "event", "event", "quantize",
                                         "event", "gemm1", "event", "gemm2", "event", "combine",
                                         "event", "copy"};
   CHECK(g_calls == nvd);
@@ -228,8 +234,8 @@ static void forward_checks() {
         NVFP4_ERR_INVALID_ARG);
   CHECK(nvfp4_moe_forward_w4a16(&w16, x, logits, T, k, nullptr, out, ws, ws16, nullptr,
                                 nullptr) == NVFP4_OK);
-  const std::vector<std::string> w16c = {"route", "permute", "gemm1", "gemm2", "combine"};
-  CHECK(g_calls == w16c && g_gemm1_mode == 1 && g_gemm2_mode == 1);
+  const std::vector<std::string> w16c = {"route", "gemm1", "gemm2", "combine"};
+  CHECK(g_calls == w16c && g_gemm1_mode == 1 && g_gemm2_mode == 1 && g_gemm1_fold);
 
   // UE8M0 mode
   g_calls.clear();
@@ -257,14 +263,13 @@ static void forward_checks() {
     g_calls.clear();
     CHECK(nvfp4_moe_forward(&wf, xf, logits, T, k, nullptr, of, wsb, wsf, nullptr, nullptr) ==
           NVFP4_OK);
-    const std::vector<std::string> nvq = {"route_quantize", "permute", "gemm1", "gemm2",
-                                          "combine"};
+    const std::vector<std::string> nvq = {"route_quantize", "gemm1", "gemm2", "combine"};
     CHECK(g_calls == nvq);
     g_calls.clear();
     CHECK(nvfp4_moe_forward(&wf, xf, logits, T, k, nullptr, of, wsb, wsf, &dbg, nullptr) ==
           NVFP4_OK);
-    const std::vector<std::string> nvqd = {"event", "route_quantize", "event", "permute",
-                                           "event", "event", "gemm1", "event", "gemm2",
+    const std::vector<std::string> nvqd = {"event", "route_quantize", "event", "event",
+                                           "event", "gemm1", "event", "gemm2",
                                            "event", "combine", "event", "copy"};
     CHECK(g_calls == nvqd);
     g_calls.clear();
@@ -277,6 +282,45 @@ static void forward_checks() {
     CHECK(nvfp4_moe_forward_w4a16(&wf16, xf, logits, T, k, nullptr, of, wsb, wsf16, nullptr,
                                   nullptr) == NVFP4_OK);
     CHECK(g_calls == w16c);
+  }
+
+  // the permute kernel stays for batches the small-batch GEMM1 does not
+  // regroup: the large-batch kernels (300 pairs on 8 experts) and more than
+  // 512 pairs (640 on 64 experts)
+  {
+    const int32_t Tl = 100;
+    void* xl = b.get((size_t)Tl * H * 2);
+    void* ol = b.get((size_t)Tl * H * 2);
+    float* ll = (float*)b.get((size_t)Tl * E * 4);
+    size_t wsl = 0;
+    CHECK(nvfp4_moe_workspace_size(Tl, k, &w, &wsl) == NVFP4_OK);
+    void* wsb = b.get(wsl);
+    g_calls.clear();
+    CHECK(nvfp4_moe_forward(&w, xl, ll, Tl, k, nullptr, ol, wsb, wsl, nullptr, nullptr) ==
+          NVFP4_OK);
+    const std::vector<std::string> kept = {"route", "permute", "quantize", "gemm1", "gemm2",
+                                           "combine"};
+    CHECK(g_calls == kept && !g_gemm1_fold);
+
+    nvfp4_moe_weights_t w64 = w;
+    const int32_t E64 = 64, T64 = 40, k64 = 16;
+    w64.num_experts = E64;
+    w64.w13 = (const uint8_t*)b.get((size_t)E64 * 2 * I * H / 2);
+    w64.w13_sf = (const uint8_t*)b.get((size_t)E64 * 2 * I * H / 16);
+    w64.w2 = (const uint8_t*)b.get((size_t)E64 * H * I / 2);
+    w64.w2_sf = (const uint8_t*)b.get((size_t)E64 * H * I / 16);
+    w64.w13_scale2 = w64.w2_scale2 = w64.w13_input_scale = w64.w2_input_scale =
+        w64.a1_gscale = w64.a2_gscale = (const float*)b.get(E64 * 4);
+    void* x64 = b.get((size_t)T64 * H * 2);
+    void* o64 = b.get((size_t)T64 * H * 2);
+    float* l64 = (float*)b.get((size_t)T64 * E64 * 4);
+    size_t ws64 = 0;
+    CHECK(nvfp4_moe_workspace_size(T64, k64, &w64, &ws64) == NVFP4_OK);
+    void* wsc = b.get(ws64);
+    g_calls.clear();
+    CHECK(nvfp4_moe_forward(&w64, x64, l64, T64, k64, nullptr, o64, wsc, ws64, nullptr,
+                            nullptr) == NVFP4_OK);
+    CHECK(g_calls == kept && !g_gemm1_fold && g_gemm1_P == T64 * k64);
   }
 
   // argument checks: nothing is launched

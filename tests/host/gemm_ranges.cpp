@@ -87,6 +87,27 @@ void check_gemm(const Case& c, bool gemm1) {
   const int32_t total = mt_prefix[E] * nt_count;
   const int32_t xcd_tiles = per_xcd(total);
 
+  // Small batches: GEMM1 regroups the routed ids itself.  The ids are laid out
+  // here as an interleaving of the experts' pairs (consistent with the
+  // counts); the per-tile ranking below repeats the kernel's walk (64 ids at a
+  // time, rank = matches before the pair) and checks that every row of every
+  // tile gets exactly one pair and every pair exactly one inverse entry.
+  const bool fold = gemm1 && fold_permutation(P, E);
+  std::vector<int32_t> ids;
+  std::vector<uint8_t> inv_written;
+  if (fold) {
+    check(sh.mb == 1 && bm == 32, "regrouping runs in the 32-row small-batch kernel");
+    check(P <= kFoldMaxPairs, "routed ids fit the workgroup's LDS copy");
+    std::vector<int32_t> left(c.counts);
+    for (int32_t q = 0, e = 0; q < P; ++q) {
+      while (left[e] == 0) e = (e + 1) % E;
+      ids.push_back(e);
+      --left[e];
+      e = (e + 7) % E;
+    }
+    inv_written.assign((size_t)P, 0);
+  }
+
   // coverage: each (m-tile, n-tile) once
   std::vector<uint8_t> seen((size_t)total, 0);
   int64_t rows_covered = 0;
@@ -101,6 +122,31 @@ void check_gemm(const Case& c, bool gemm1) {
     check(tl.row0 >= offsets[tl.e] && tl.row0 + tl.rows <= offsets[tl.e + 1],
           "tile rows inside the expert's rows");
     if (tl.nt == 0) rows_covered += tl.rows;
+    if (fold) {
+      check_range("routed ids read", 0, P, (int64_t)ids.size());
+      check_range("offsets written", 0, E + 1, (int64_t)offsets.size());
+      check(tl.rows <= 32, "tile rows fit the per-tile pair list");
+      const int32_t lo = tl.row0 - offsets[tl.e];
+      std::vector<int32_t> src((size_t)tl.rows, -1);
+      int32_t matches = 0;
+      for (int32_t c0 = 0; c0 < P; c0 += 64)
+        for (int lane = 0; lane < 64; ++lane) {
+          const int32_t q = c0 + lane;
+          if (q >= P || ids[q] != tl.e) continue;
+          const int32_t r = matches++ - lo;
+          if (r >= 0 && r < tl.rows) {
+            check(src[r] < 0, "tile row ranked once");
+            src[r] = q;
+          }
+        }
+      for (int32_t r = 0; r < tl.rows; ++r) {
+        check(src[r] >= 0 && src[r] < P, "every tile row has a pair in [0, P)");
+        if (tl.nt == 0 && src[r] >= 0 && src[r] < P) {
+          check_range("src_pair written", tl.row0 + r, tl.row0 + r + 1, P);
+          check(inv_written[src[r]]++ == 0, "inv entry written once");
+        }
+      }
+    }
     const int sub = (tl.rows + 31) >> 5;
     const int mba = sub >= sh.mb ? sh.mb : sub;   // occupied 32-row sub-tiles staged
 
@@ -196,6 +242,7 @@ void check_gemm(const Case& c, bool gemm1) {
   }
   for (int32_t i = 0; i < total; ++i) check(seen[i] == 1, "every tile visited once");
   check(rows_covered == P, "n-tile 0 covers every grouped row once");
+  for (size_t q = 0; q < inv_written.size(); ++q) check(inv_written[q] == 1, "every pair gets inv");
 }
 
 }  // namespace
