@@ -336,9 +336,10 @@ typedef struct {
  * array of NVFP4_MOE_STAGES+1 hipEvent_t (created by the caller) recorded on
  * the stream before the first launch and after each stage: route, permute,
  * quantise A1, grouped w13 GEMM (+SiLU*mul+requant), grouped w2 GEMM,
- * combine.  In the E4M3 forward, when H/16 lies in [64, 1024], routing and
- * the A1 quantisation run as one kernel: it is timed as the route stage and
- * the quantise stage is empty.  Batches of at most 512 pairs whose experts
+ * combine.  In the W4A4 forwards, when H/16 lies in [64, 1024] (and H is a
+ * multiple of 128 in the UE8M0 mode), routing and the A1 quantisation run as
+ * one kernel: it is timed as the route stage and the quantise stage is
+ * empty.  Batches of at most 512 pairs whose experts
  * average fewer than 32 rows (P < 32*E) launch no permutation kernel: the
  * w13 GEMM regroups the routed ids itself and writes expert_offsets,
  * src_pair and inv, so the permute stage is empty.  Buffer dumps are copied

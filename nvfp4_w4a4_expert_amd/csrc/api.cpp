@@ -390,14 +390,14 @@ nvfp4_status_t moe_forward(const nvfp4_moe_weights_t* w, const void* x_bf16,
   };
   hipError_t err = mark(0);
   // A1 rows are written in (token, slot) order q = t*k + j: each token's k
-  // rows are contiguous, and GEMM1 reads them through src_pair.  The E4M3
-  // mode routes and quantises in one kernel where the fused kernel covers
+  // rows are contiguous, and GEMM1 reads them through src_pair.  Both W4A4
+  // modes route and quantise in one kernel where the fused kernel covers
   // the shape (timed as the route stage; the quantise stage is then empty).
   bool fused = false;
-  if (err == hipSuccess && !w16 && !mx) {
+  if (err == hipSuccess && !w16) {
     const hipError_t ferr = launch_route_quantize(
         router_logits, T, E, k, ids, wts, static_cast<const uint16_t*>(x_bf16), H,
-        w->a1_gscale, a1c, a1s, s);
+        w->a1_gscale, a1c, a1s, s, mx);
     if (ferr == hipSuccess) fused = true;
     else if (ferr != hipErrorNotSupported) err = ferr;
   }

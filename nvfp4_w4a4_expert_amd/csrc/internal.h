@@ -26,14 +26,15 @@ hipError_t launch_quantize_gather(const uint16_t* x, int64_t ldx, int32_t K,
 hipError_t launch_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* ids,
                         float* weights, hipStream_t stream);
 
-// The router and the layer's A1 quantisation (bf16 x [T, H], E4M3 scales,
-// rows in (token, slot) order) in one launch.  Returns hipErrorNotSupported,
-// launching nothing, for shapes it does not cover (H/16 below 64 or above
-// 1024, k above 32); the caller then launches the two kernels.
+// The router and the layer's A1 quantisation (bf16 x [T, H], E4M3 scales per
+// 16 elements, or UE8M0 scales per 32 when mx; rows in (token, slot) order)
+// in one launch.  Returns hipErrorNotSupported, launching nothing, for shapes
+// it does not cover (H/16 below 64 or above 1024, k above 32); the caller
+// then launches the two kernels.
 hipError_t launch_route_quantize(const float* logits, int32_t T, int32_t E, int32_t k,
                                  int32_t* ids, float* weights, const uint16_t* x, int32_t H,
                                  const float* gscale, uint8_t* codes, uint8_t* sf,
-                                 hipStream_t stream);
+                                 hipStream_t stream, bool mx = false);
 
 hipError_t launch_permute(const int32_t* ids, int32_t P, int32_t E, int32_t* offsets,
                           int32_t* src_pair, int32_t* inv, hipStream_t stream);

@@ -135,7 +135,12 @@ __global__ __launch_bounds__(1024) void quantize_experts_kernel(
 // -> 28.5 us; storing each slot as soon as it is encoded leaves the stores
 // spread between the encoding instructions).  kTopk > 0 fixes the slot count
 // at compile time.
-template <bool kP, int kTopk>
+// kMX: UE8M0 block scales, one per 32 elements (page 3, "NVFP4" section, the
+// quantiser template's UE8M0_SF switch).  The two 16-element halves of a
+// block are lanes b and b ^ 1, which share the block's absolute maximum; the
+// lanes at multiples of 8 store the 4 scale bytes of blocks b/2 .. b/2 + 3
+// as one 32-bit word (nblk must then be a multiple of 8).
+template <bool kP, int kTopk, bool kMX = false>
 __device__ __forceinline__ void quantize_token_slots(
     const uint16_t* __restrict__ x_row, int32_t nblk, int32_t b, int32_t topk_arg,
     const int32_t* tok_ids, const int32_t* tok_dst, int32_t q0, int32_t num_experts,
@@ -149,7 +154,9 @@ __device__ __forceinline__ void quantize_token_slots(
   const u32x4 v1 = __builtin_nontemporal_load(src + 1);
   unpack_bf16x8(v0, xv);
   unpack_bf16x8(v1, xv + 8);
-  const float a6 = absmax16(xv) / kE2M1Max;
+  float am = absmax16(xv);
+  if constexpr (kMX) am = fmaxf(am, __shfl_xor(am, 1, 64));   // the block's other half
+  const float a6 = am / kE2M1Max;
   const uint32_t row_bytes = (uint32_t)nblk * 8u;
   constexpr int kBatch = 8;
   for (int32_t j0 = 0; j0 < topk; j0 += kBatch) {
@@ -174,19 +181,33 @@ __device__ __forceinline__ void quantize_token_slots(
     uint32_t sw[kBatch];
 #pragma unroll
     for (int jj = 0; jj < kBatch; ++jj) {
-      const BlockScale bs = block_scale(a6, gb[jj]);
+      const BlockScale bs = kMX ? block_scale_ue8m0(a6, gb[jj]) : block_scale(a6, gb[jj]);
       w[jj].x = encode8(xv, bs.inv);
       w[jj].y = encode8(xv + 8, bs.inv);
       uint32_t v = bs.sf;
-      v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false) << 8;
-      v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false) << 16;
+      if constexpr (kMX) {
+        // lanes b + 2, b + 4 and b + 6 hold the next three blocks' scales
+        v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false) << 8;
+        v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x104, 0xF, 0xF, false) << 16;
+      } else {
+        v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false) << 8;
+        v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false) << 16;
+      }
       sw[jj] = v;
     }
 #pragma unroll
     for (int jj = 0; jj < kBatch; ++jj)
       if (keep[jj])
         *reinterpret_cast<uint2*>(codes + ((uint32_t)pb[jj] * row_bytes + (uint32_t)b * 8u)) = w[jj];
-    if ((b & 3) == 0) {
+    if constexpr (kMX) {
+      if ((b & 7) == 0) {
+#pragma unroll
+        for (int jj = 0; jj < kBatch; ++jj)
+          if (keep[jj])
+            *reinterpret_cast<uint32_t*>(
+                sf + ((uint32_t)pb[jj] * (uint32_t)(nblk / 2) + (uint32_t)(b / 2))) = sw[jj];
+      }
+    } else if ((b & 3) == 0) {
 #pragma unroll
       for (int jj = 0; jj < kBatch; ++jj)
         if (keep[jj])
@@ -196,7 +217,7 @@ __device__ __forceinline__ void quantize_token_slots(
   }
 }
 
-template <bool kP, int kTopk>
+template <bool kP, int kTopk, bool kMX>
 __global__ __launch_bounds__(1024) void quantize_pairs_fast_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int32_t nblk, int32_t topk,
     const int32_t* __restrict__ expert_idx, const int32_t* __restrict__ dst_row,
@@ -204,9 +225,9 @@ __global__ __launch_bounds__(1024) void quantize_pairs_fast_kernel(
     uint8_t* __restrict__ sf, int32_t num_dst_rows) {
   const int32_t t = (int32_t)blockIdx.x;
   const int64_t q0 = (int64_t)t * (kTopk > 0 ? kTopk : topk);
-  quantize_token_slots<kP, kTopk>(x + (int64_t)t * ldx, nblk, (int32_t)threadIdx.x, topk,
-                                  expert_idx + q0, kP ? dst_row + q0 : nullptr, (int32_t)q0,
-                                  num_experts, gscale, codes, sf, num_dst_rows);
+  quantize_token_slots<kP, kTopk, kMX>(x + (int64_t)t * ldx, nblk, (int32_t)threadIdx.x, topk,
+                                       expert_idx + q0, kP ? dst_row + q0 : nullptr, (int32_t)q0,
+                                       num_experts, gscale, codes, sf, num_dst_rows);
 }
 
 // Routing and the A1 quantisation of the layer in one launch: workgroup t
@@ -214,8 +235,8 @@ __global__ __launch_bounds__(1024) void quantize_pairs_fast_kernel(
 // router's own code, route_token) and writes the token's k ids and weights;
 // after a barrier every lane quantises its block of the row into rows
 // t*k + j with the SFScaleVals of the picked experts.  This saves the
-// router's launch.
-template <int EPL, int kTopk>
+// router's launch.  kMX: UE8M0 block scales per 32 elements.
+template <int EPL, int kTopk, bool kMX>
 __global__ __launch_bounds__(1024) void route_quantize_kernel(
     const float* __restrict__ logits, int32_t E, int32_t k_arg, int32_t* __restrict__ ids,
     float* __restrict__ weights, const uint16_t* __restrict__ x, int32_t nblk,
@@ -236,8 +257,9 @@ __global__ __launch_bounds__(1024) void route_quantize_kernel(
     }
   }
   __syncthreads();
-  quantize_token_slots<false, kTopk>(x + (int64_t)t * nblk * 16, nblk, (int32_t)threadIdx.x, k,
-                                     s_ids, nullptr, t * k, E, gscale, codes, sf, num_dst_rows);
+  quantize_token_slots<false, kTopk, kMX>(x + (int64_t)t * nblk * 16, nblk, (int32_t)threadIdx.x,
+                                          k, s_ids, nullptr, t * k, E, gscale, codes, sf,
+                                          num_dst_rows);
 }
 
 // Gather form: one workgroup per destination row p (grid.x) and one 16-element
@@ -357,7 +379,8 @@ hipError_t launch_quantize(const uint16_t* x, int64_t ldx, int32_t num_rows, int
     // 28.8 us on the 8192 x 2816 workload with destinations in token-slot
     // order)
 #define NVFP4_FAST(kp, kk)                                                                       \
-  hipLaunchKernelGGL((quantize_pairs_fast_kernel<kp, kk>), dim3((uint32_t)num_rows), dim3(nblk), \
+  hipLaunchKernelGGL((quantize_pairs_fast_kernel<kp, kk, false>), dim3((uint32_t)num_rows),      \
+                     dim3(nblk),                                                                 \
                      0, stream, x, ldx, nblk, topk, expert_idx, dst_row, num_experts, gscale,    \
                      codes, sf, num_dst_rows)
     if (dst_row) {
@@ -603,16 +626,22 @@ hipError_t launch_conversions_selftest(unsigned long long* count, hipStream_t st
 hipError_t launch_route_quantize(const float* logits, int32_t T, int32_t E, int32_t k,
                                  int32_t* ids, float* weights, const uint16_t* x, int32_t H,
                                  const float* gscale, uint8_t* codes, uint8_t* sf,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, bool mx) {
   const int32_t nblk = H / 16;
-  if (T < 1 || E < 1 || E > 1024 || k < 1 || k > 32 || k > E || H % 64 || nblk < 64 ||
-      nblk > 1024 || !gscale || (reinterpret_cast<uintptr_t>(sf) & 3) != 0 ||
+  // whole scale words: 4 E4M3 scales (H % 64), or 4 UE8M0 scales of 32
+  // elements (H % 128)
+  if (T < 1 || E < 1 || E > 1024 || k < 1 || k > 32 || k > E || H % (mx ? 128 : 64) ||
+      nblk < 64 || nblk > 1024 || !gscale || (reinterpret_cast<uintptr_t>(sf) & 3) != 0 ||
       (int64_t)T * k * nblk * 8 > (int64_t)UINT32_MAX)
     return hipErrorNotSupported;
   const int32_t P = T * k;
 #define NVFP4_RQ(epl, kk)                                                                        \
-  hipLaunchKernelGGL((route_quantize_kernel<epl, kk>), dim3((uint32_t)T), dim3(nblk), 0, stream,  \
-                     logits, E, k, ids, weights, x, nblk, gscale, codes, sf, P)
+  if (mx)                                                                                        \
+    hipLaunchKernelGGL((route_quantize_kernel<epl, kk, true>), dim3((uint32_t)T), dim3(nblk), 0,  \
+                       stream, logits, E, k, ids, weights, x, nblk, gscale, codes, sf, P);       \
+  else                                                                                           \
+    hipLaunchKernelGGL((route_quantize_kernel<epl, kk, false>), dim3((uint32_t)T), dim3(nblk), 0, \
+                       stream, logits, E, k, ids, weights, x, nblk, gscale, codes, sf, P)
 #define NVFP4_RQ_E(kk)                                                                           \
   if (E <= 64) NVFP4_RQ(1, kk);                                                                  \
   else if (E <= 128) NVFP4_RQ(2, kk);                                                            \

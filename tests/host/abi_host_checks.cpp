@@ -24,6 +24,8 @@ static int g_quant_mx = -1, g_gemm1_mode = -1, g_gemm2_mode = -1;
 static int32_t g_gemm1_P = -1, g_quant_dst_rows = -1;
 // GEMM1 asked to regroup the routed ids itself (the permute kernel skipped)
 static bool g_gemm1_fold = false;
+// the fused routing + A1 quantisation launched in the UE8M0 mode
+static bool g_rq_mx = false;
 static int g_gather_src_div = -1;
 
 namespace nvfp4 {
@@ -49,12 +51,13 @@ hipError_t launch_route(const float*, int32_t, int32_t, int32_t, int32_t*, float
 }
 hipError_t launch_route_quantize(const float*, int32_t T, int32_t E, int32_t k, int32_t*,
                                  float*, const uint16_t*, int32_t H, const float* gscale,
-                                 uint8_t* codes, uint8_t* sf, hipStream_t) {
+                                 uint8_t* codes, uint8_t* sf, hipStream_t, bool mx) {
   // the shapes the real launcher covers; otherwise nothing is launched
-  if (T < 1 || E > 1024 || k > 32 || H % 64 || H / 16 < 64 || H / 16 > 1024)
+  if (T < 1 || E > 1024 || k > 32 || H % (mx ? 128 : 64) || H / 16 < 64 || H / 16 > 1024)
     return hipErrorNotSupported;
   if (!gscale || !codes || !sf) abort();
   g_calls.push_back("route_quantize");
+  g_rq_mx = mx;
   return hipSuccess;
 }
 hipError_t launch_permute(const int32_t*, int32_t, int32_t, int32_t*, int32_t*, int32_t*,
@@ -244,8 +247,8 @@ static void forward_checks() {
   CHECK(g_calls == nv && g_quant_mx == 1 && g_gemm1_mode == 2 && g_gemm2_mode == 2);
 
   // hidden 1024 (H/16 = 64): routing and the A1 quantisation in one kernel,
-  // timed as the route stage; the weight-only and UE8M0 modes keep the
-  // separate router
+  // timed as the route stage, in both W4A4 modes; the weight-only mode keeps
+  // the separate router
   {
     nvfp4_moe_weights_t wf = w;
     const int32_t Hf = 1024;
@@ -271,11 +274,12 @@ static void forward_checks() {
     const std::vector<std::string> nvqd = {"event", "route_quantize", "event", "event",
                                            "event", "gemm1", "event", "gemm2",
                                            "event", "combine", "event", "copy"};
-    CHECK(g_calls == nvqd);
+    CHECK(g_calls == nvqd && !g_rq_mx);
+    // the UE8M0 mode fuses its routing and A1 quantisation the same way
     g_calls.clear();
     CHECK(nvfp4_moe_forward_mx(&wf, xf, logits, T, k, nullptr, of, wsb, wsf, nullptr,
                                nullptr) == NVFP4_OK);
-    CHECK(g_calls == nv && g_quant_mx == 1);
+    CHECK(g_calls == nvq && g_rq_mx && g_gemm1_mode == 2);
     nvfp4_moe_weights_t wf16 = wf;
     wf16.w13_input_scale = wf16.w2_input_scale = wf16.a1_gscale = wf16.a2_gscale = nullptr;
     g_calls.clear();

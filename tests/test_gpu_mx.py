@@ -160,6 +160,22 @@ def test_mx_determinism():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("E,k,T", [(64, 1, 5), (256, 32, 9), (512, 4, 33), (1024, 8, 3)])
+def test_mx_fused_routing_and_quantisation(E, k, T):
+    """The UE8M0 mode's fused routing + A1 quantisation (one launch) at
+    hidden 1024, the narrowest row it takes, with expert counts that select
+    each router width and top-k other than 8 as well as 8: ids, weights,
+    permutation, A1 codes and power-of-two scales exactly, the rest within
+    the bounds."""
+    w = S.Workload(f"mx-fused-E{E}-k{k}", 8, T=T, H=1024, E=E, I=64, k=k, router="normal",
+                   calib_tokens=2048)
+    w13, w2 = S.expert_weights(w)
+    layer = OX.prepare_layer(w13, w2, *S.calibration_batch(w), k, threads=16)
+    del w13, w2
+    m = check_layer_parity(layer, S.activations(w), S.router_logits(w), k, label=w.name, mx=True)
+    _report(w.name, m)
+
+
 @pytest.mark.timeout(900)
 def test_mx_decode_layer():
     w = S.WORKLOADS["decode"]
