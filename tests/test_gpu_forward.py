@@ -88,6 +88,22 @@ def test_decode_layer():
     _report("decode", m)
 
 
+@pytest.mark.parametrize("T", [64, 65])
+def test_permutation_fold_threshold(T):
+    """The decode layer's shape at 64 tokens (512 pairs: the most the
+    small-batch w13 GEMM regroups itself, its LDS copy of the ids full) and
+    at 65 tokens (520 pairs: the permutation kernel runs again), both on the
+    small-batch GEMMs: ids, offsets, src_pair and inv exactly, the rest
+    within the bounds."""
+    w = S.WORKLOADS["decode"]
+    rng = np.random.default_rng(640 + T)
+    x = S.f32_to_bf16_bits(rng.standard_normal((T, w.H)).astype(np.float32))
+    logits = rng.standard_normal((T, w.E)).astype(np.float32)
+    assert T * w.k < 32 * w.E                           # small-batch kernels
+    m = check_layer_parity(oracle_layer("decode"), x, logits, w.k, label=f"fold T={T}")
+    _report(f"fold T={T}", m)
+
+
 @pytest.mark.timeout(900)
 def test_prefill_layer():
     w = S.WORKLOADS["prefill"]
