@@ -344,6 +344,8 @@ def bench_decode(args, torch, M, L, events, layers):
                 us_per_step_instrumented=round(ms_i * 1000, 2), experts_hit=round(n_hit, 1),
                 weight_bytes_per_step=int(n_hit * per_expert),
                 layer_weight_gbps=round(n_hit * per_expert / (ms * 1e-3) / 1e9, 1),
+                # the whole step against the time the hit experts' weights take at peak HBM
+                layer_frac_of_hbm_peak=round(n_hit * per_expert / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                 gemm1_weight_gbps=round(g1_bytes / (g1 * 1e-6) / 1e9, 1),
                 gemm1_frac_of_hbm_peak=round(g1_bytes / (g1 * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                 stages_us={k_: round(v, 2) for k_, v in st.items()})
