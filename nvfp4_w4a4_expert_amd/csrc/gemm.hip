@@ -919,7 +919,7 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t stream) {
     return launch_shape<kModeNV, kG1Large>(prm, a.P, stream);
   }
   if (mode == kModeMX) return launch_shape<kModeMX, kG1SmallMx>(prm, a.P, stream);
-  if (mode == kModeW16) return launch_shape<kModeW16, kG1Small>(prm, a.P, stream);
+  if (mode == kModeW16) return launch_shape<kModeW16, kG1SmallW16>(prm, a.P, stream);
   return launch_shape<kModeNV, kG1Small>(prm, a.P, stream);
 }
 
@@ -938,8 +938,8 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t stream) {
     if (mode == kModeW16) return launch_shape<kModeW16, kG2Large>(prm, a.P, stream);
     return launch_shape<kModeNV, kG2Large>(prm, a.P, stream);
   }
-  if (mode == kModeMX) return launch_shape<kModeMX, kG2Small>(prm, a.P, stream);
-  if (mode == kModeW16) return launch_shape<kModeW16, kG2Small>(prm, a.P, stream);
+  if (mode == kModeMX) return launch_shape<kModeMX, kG2SmallMx>(prm, a.P, stream);
+  if (mode == kModeW16) return launch_shape<kModeW16, kG2SmallW16>(prm, a.P, stream);
   return launch_shape<kModeNV, kG2Small>(prm, a.P, stream);
 }
 
@@ -993,8 +993,10 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restr
 int32_t weight_step_k(int32_t projection, bool mx) {
   // every GEMM1 shape of a mode shares one K step, as every GEMM2 shape does
   static_assert(kG1Large.bk == kG1Small.bk && kG1Large.bk == kG1LargeW16.bk &&
-                kG1LargeMx.bk == kG1SmallMx.bk, "one w13 K step per mode");
-  static_assert(kG2Large.bk == kG2Small.bk && kG2Large.bk == kG2LargeMx.bk,
+                kG1Large.bk == kG1SmallW16.bk && kG1LargeMx.bk == kG1SmallMx.bk,
+                "one w13 K step per mode");
+  static_assert(kG2Large.bk == kG2Small.bk && kG2Large.bk == kG2LargeMx.bk &&
+                kG2Large.bk == kG2SmallW16.bk && kG2Large.bk == kG2SmallMx.bk,
                 "one w2 K step");
   return projection == 0 ? (mx ? kG1LargeMx.bk : kG1Large.bk) : kG2Large.bk;
 }

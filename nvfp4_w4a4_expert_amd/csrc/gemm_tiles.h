@@ -62,10 +62,23 @@ constexpr Shape kG2Large{4, 4, 64, 2, 2, false};
 // ring fits in 247 VGPRs; measured 138 -> 136 us; in the other modes it spills)
 constexpr Shape kG2LargeMx{4, 4, 64, 3, 2, false};
 // Batches with fewer than 32 rows per expert on average (decode): one 32-row
-// sub-tile, 4 wavefronts, 2 workgroups per CU, 3-slot rings.
-constexpr Shape kG1Small{4, 1, 128, 3, 2, true};
+// sub-tile and 4 wavefronts; each tile streams one expert's weight slice, so
+// the more workgroups a CU holds, the more of those streams are in flight.
+// E4M3 mode: w13 with a 2-slot ring at 3 workgroups per CU (164 VGPRs), w2
+// with a 3-slot ring at 4 per CU (128 VGPRs), so that the 16-token decode
+// layer's ~880 w2 tiles (80 hit experts x 11 column tiles) run in one round
+// of 1024 slots instead of 768 (measured: decode step 68.7 -> 65.7 us).
+constexpr Shape kG1Small{4, 1, 128, 2, 3, true};
+constexpr Shape kG2Small{4, 1, 64, 3, 4, false};
+// UE8M0 mode: w2 with a 2-slot ring at 4 workgroups per CU (125 VGPRs;
+// decode step 58.6 -> 56.8 us); its w13 keeps a 3-slot ring at 2 per CU (a
+// 2-slot ring at 3 per CU spills and was slower).  Weight-only mode: 3-slot
+// rings at 2 workgroups per CU (2-slot rings at 3 and 4 per CU spill and
+// gained nothing measurable).
 constexpr Shape kG1SmallMx{4, 1, 256, 3, 2, true};
-constexpr Shape kG2Small{4, 1, 64, 3, 2, false};
+constexpr Shape kG2SmallMx{4, 1, 64, 2, 4, false};
+constexpr Shape kG1SmallW16{4, 1, 128, 3, 2, true};
+constexpr Shape kG2SmallW16{4, 1, 64, 3, 2, false};
 
 // The large-batch kernels run when experts average at least 32 rows.
 NVFP4_HD bool large_batch(int32_t P, int32_t E) { return P >= 32 * E; }
@@ -85,8 +98,8 @@ NVFP4_HD Shape select_shape(bool gemm1, int mode, int32_t P, int32_t E) {
     if (gemm1) return mode == kModeMX ? kG1LargeMx : mode == kModeW16 ? kG1LargeW16 : kG1Large;
     return mode == kModeMX ? kG2LargeMx : kG2Large;
   }
-  if (gemm1) return mode == kModeMX ? kG1SmallMx : kG1Small;
-  return kG2Small;
+  if (gemm1) return mode == kModeMX ? kG1SmallMx : mode == kModeW16 ? kG1SmallW16 : kG1Small;
+  return mode == kModeMX ? kG2SmallMx : mode == kModeW16 ? kG2SmallW16 : kG2Small;
 }
 
 // n-tiles of a launch: GEMM1 tiles cover 32 h columns per wavefront (32 gate
