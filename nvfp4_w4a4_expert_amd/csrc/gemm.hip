@@ -239,26 +239,24 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void grouped_gemm_kernel(
         lds_barrier();
       }
     }
-    int32_t cnt[kPer], rcnt[kPer], total = 0, rtotal = 0;
+    int32_t m[kPer], cnt[kPer], rcnt[kPer], total, rtotal;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int32_t e = kPer * tid + i;
-      int32_t m = 0;
+      m[i] = 0;
       if (e < prm.E) {
         if (fold) {
-          m = s_mt[e];
+          m[i] = s_mt[e];
         } else {
           const int32_t o0 = prm.offsets[e], o1 = prm.offsets[e + 1];
           s_off[e] = o0;
           if (e == prm.E - 1) s_off[prm.E] = o1;
-          m = o1 - o0;
+          m[i] = o1 - o0;
         }
       }
-      cnt[i] = (m + kBM - 1) / kBM;
-      rcnt[i] = m;
-      total += cnt[i];
-      rtotal += m;
     }
+    // (the same per-thread counting as the host range checker repeats)
+    thread_prefix_counts<kPer>(m, kBM, cnt, rcnt, total, rtotal);
     int32_t incl = total, rincl = rtotal;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {

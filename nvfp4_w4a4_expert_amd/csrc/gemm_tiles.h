@@ -153,6 +153,24 @@ NVFP4_HD Tile tile_of(int32_t logical, int32_t n_tiles_, const int32_t* mt_prefi
   return c;
 }
 
+// Per-thread part of a workgroup's expert prefix pass: a thread owns kPer
+// consecutive experts with m[i] rows each (0 past the last expert).  cnt[i]
+// is the expert's m-tiles of bm rows; rcnt[i] its rows (the second scan, run
+// when the small-batch GEMM1 regroups the routed ids).  The totals feed the
+// workgroup's exclusive scans.
+template <int kPer>
+NVFP4_HD void thread_prefix_counts(const int32_t (&m)[kPer], int32_t bm, int32_t (&cnt)[kPer],
+                                   int32_t (&rcnt)[kPer], int32_t& total, int32_t& rtotal) {
+  total = 0;
+  rtotal = 0;
+  for (int i = 0; i < kPer; ++i) {
+    cnt[i] = m_tiles(m[i], bm);
+    rcnt[i] = m[i];
+    total += cnt[i];
+    rtotal += rcnt[i];
+  }
+}
+
 // The two 32-row weight blocks a wavefront streams.  GEMM1: block 0 = the
 // gate rows of h columns [hc0, hc0 + 32), block 1 = the matching up rows
 // (I + hc0); GEMM2: output columns [n0, n0 + 64) as two blocks.  A wavefront

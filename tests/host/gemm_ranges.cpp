@@ -53,6 +53,40 @@ struct Case {
   std::vector<int32_t> counts;
 };
 
+// The kernel's expert prefix pass, repeated on the host: each of `threads`
+// threads owns kPer experts and counts them with the kernel's own
+// thread_prefix_counts; an exclusive scan over the threads' totals (what the
+// kernel's wavefront scans and cross-wavefront sums compute) gives each
+// thread's bases, then each owned expert's entries.
+template <int kPer>
+void kernel_prefix(const std::vector<int32_t>& counts, int32_t E, int32_t bm, int threads,
+                   std::vector<int32_t>& pre, std::vector<int32_t>& rpre) {
+  check(kPer * threads >= E + 1, "the prefix pass covers experts 0 .. E");
+  pre.assign((size_t)E + 1, -1);
+  rpre.assign((size_t)E + 1, -1);
+  int32_t base = 0, rbase = 0;
+  for (int tid = 0; tid < threads; ++tid) {
+    int32_t m[kPer], cnt[kPer], rcnt[kPer], total, rtotal;
+    for (int i = 0; i < kPer; ++i) {
+      const int32_t e = kPer * tid + i;
+      m[i] = e < E ? counts[e] : 0;
+    }
+    thread_prefix_counts<kPer>(m, bm, cnt, rcnt, total, rtotal);
+    int32_t b = base, rb = rbase;
+    for (int i = 0; i < kPer; ++i) {
+      const int32_t e = kPer * tid + i;
+      if (e <= E) {
+        pre[e] = b;
+        rpre[e] = rb;
+      }
+      b += cnt[i];
+      rb += rcnt[i];
+    }
+    base += total;
+    rbase += rtotal;
+  }
+}
+
 // One GEMM launch of a case: GEMM1 (w13, gated) or GEMM2 (w2).
 void check_gemm(const Case& c, bool gemm1) {
   const bool mx = c.mode == kModeMX, w16 = c.mode == kModeW16;
@@ -86,6 +120,17 @@ void check_gemm(const Case& c, bool gemm1) {
   check(mt_prefix[E] <= m_tiles_bound(P, E, bm), "m-tile bound sizes the grid");
   const int32_t total = mt_prefix[E] * nt_count;
   const int32_t xcd_tiles = per_xcd(total);
+  // the m-tile prefix and (small-batch GEMM1) the expert offsets as the
+  // kernel's own prefix pass computes them
+  {
+    std::vector<int32_t> kpre, krpre;
+    const int per = (kMaxExperts + 1 + threads - 1) / threads;
+    if (per == 3) kernel_prefix<3>(c.counts, E, bm, threads, kpre, krpre);
+    else if (per == 5) kernel_prefix<5>(c.counts, E, bm, threads, kpre, krpre);
+    else check(false, "experts per thread of the prefix pass");
+    check(kpre == mt_prefix, "kernel prefix pass: m-tiles");
+    check(krpre == offsets, "kernel prefix pass: expert offsets");
+  }
 
   // Small batches: GEMM1 regroups the routed ids itself.  The ids are laid out
   // here as an interleaving of the experts' pairs (consistent with the
