@@ -63,6 +63,12 @@ def _cases():
                        calib_tokens=2048)
         ids, _ = OM.route(S.router_logits(w), k)
         add(w.name, E, 1024, 64, k, T, np.bincount(ids.reshape(-1), minlength=E))
+    # the non-power-of-two expert count of the odd-expert parity tests
+    for T in (2200, 40):
+        w = S.Workload(f"odd-E200-T{T}", 9, T=T, H=1024, E=200, I=192, k=6, router="normal",
+                       calib_tokens=2048)
+        ids, _ = OM.route(S.router_logits(w), w.k)
+        add(w.name, w.E, w.H, w.I, w.k, T, np.bincount(ids.reshape(-1), minlength=w.E))
     t = S.WORKLOADS["tiny"]
     for label, counts in TILE_COUNTS.items():
         add(f"tiles-{label}", t.E, t.H, t.I, 1, sum(counts), counts)
