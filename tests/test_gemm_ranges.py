@@ -78,6 +78,8 @@ def _cases():
     add("switch-at", 4, 256, 128, 1, 128, [32, 32, 32, 32])
     add("switch-below", 4, 256, 128, 1, 127, [32, 32, 32, 31])
     add("single-expert", 1, 512, 192, 1, 77, [77])
+    for T in (5, 300):                        # the single-expert GPU parity shapes
+        add(f"single-expert-T{T}", 1, 256, 128, 1, T, [T])
     add("single-row", 8, 256, 64, 1, 1, [0, 0, 0, 0, 0, 0, 0, 1])
     add("wide-empty", 1024, 256, 128, 1, 3, [1] + [0] * 1021 + [1, 1])
     return cases
